@@ -1,0 +1,373 @@
+"""Pins of the FP64 oracle against things other than itself (CPU only).
+
+The pages print no worked example (no input values with their outputs), so every pin is a
+closed form, an invariant of the mathematics, an independent re-formulation, a library
+routine on a special case, or exact brute force on tiny inputs.  Each is chosen so that a
+plausible mistake in the oracle (a dropped term, a wrong sign, the decay in the wrong place,
+the output read before the update, a transposed state, the wrong key head) fails at least
+one of them.
+
+Sources: "#413 prefill: DeltaNet recurrence with the three value heads of a key head in one
+thread" (sections "What changes", "Exactness") and "#1372 DeltaNet recurrence:
+STRATA_GDN_CHUNKED=1" (section "What it does").
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import rel_err
+from linear_attention_recurrence_gated_amd.inputs import EDGE_LENGTHS, make_inputs
+from oracle import forms
+
+
+def _small(T, seed=0, hk=2, hv=6, dk=128, dv=128, **kw):
+    return make_inputs(T, seed=seed, n_k_heads=hk, n_v_heads=hv, dk=dk, dv=dv, **kw)
+
+
+def _run(oracle_mod, x, heads=None):
+    return oracle_mod.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], heads=heads)
+
+
+# --- P-a: brute force in the dense per-token matrix form -------------------------------
+
+def test_dense_form_full_heads(oracle_mod):
+    x = make_inputs(24, seed=3)
+    o, s = _run(oracle_mod, x)
+    od, sd = forms.recurrence_dense(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    assert rel_err(o, od) < 1e-13
+    assert rel_err(s, sd) < 1e-13
+
+
+def test_dense_form_longer(oracle_mod):
+    x = _small(64, seed=4)
+    o, s = _run(oracle_mod, x)
+    od, sd = forms.recurrence_dense(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    assert rel_err(o, od) < 1e-13
+    assert rel_err(s, sd) < 1e-13
+
+
+# --- P-b: the chunked WY form (library solve) for several chunk sizes -------------------
+
+@pytest.mark.parametrize("C", [1, 7, 32, 64])
+@pytest.mark.parametrize("T", [1, 5, 31, 33])
+def test_wy_form_full_heads(oracle_mod, C, T):
+    x = make_inputs(T, seed=T)
+    o, s = _run(oracle_mod, x)
+    ow, sw = forms.recurrence_wy(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], C=C)
+    assert rel_err(o, ow) < 1e-12
+    assert rel_err(s, sw) < 1e-12
+
+
+@pytest.mark.parametrize("T", EDGE_LENGTHS)
+def test_wy_form_edge_lengths(oracle_mod, T):
+    x = _small(T, seed=100 + T)
+    o, s = _run(oracle_mod, x)
+    ow, sw = forms.recurrence_wy(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], C=32)
+    assert rel_err(o, ow) < 1e-12
+    assert rel_err(s, sw) < 1e-12
+
+
+def test_wy_exclusive_prefix_would_fail(oracle_mod):
+    """The WY form reproduces the recurrence only with the inclusive running sum of the
+    gate; shifting gamma by one token (the exclusive reading) must be detectably wrong."""
+    x = _small(40, seed=9)
+    o, _ = _run(oracle_mod, x)
+    g_shift = np.concatenate([np.zeros((1, x["g"].shape[1]), np.float32), x["g"][:-1]])
+    ow, _ = forms.recurrence_wy(x["q"], x["k"], x["v"], g_shift, x["beta"], x["s0"], C=32)
+    assert rel_err(ow, o) > 1e-3
+
+
+# --- P-c: T = 1 closed forms --------------------------------------------------------------
+
+def test_t1_closed_form(oracle_mod):
+    x = _small(1, seed=5)
+    o, s = _run(oracle_mod, x)
+    for h in range(6):
+        kh = h % 2
+        S0 = x["s0"][h].astype(np.float64)
+        kk = x["k"][0, kh].astype(np.float64)
+        qq = x["q"][0, kh].astype(np.float64)
+        vv = x["v"][0, h].astype(np.float64)
+        a = np.exp(np.float64(x["g"][0, h]))
+        b = np.float64(x["beta"][0, h])
+        S1 = a * S0 + np.outer(kk, b * (vv - a * (S0.T @ kk)))
+        assert rel_err(s[h], S1) < 1e-15
+        assert rel_err(o[0, h], S1.T @ qq) < 1e-14
+
+
+def test_t1_zero_state_gives_scaled_value(oracle_mod):
+    """From S0 = 0 one token gives o = beta (q.k) v: the output sees the token's own write."""
+    x = _small(1, seed=6)
+    x["s0"][:] = 0
+    o, _ = _run(oracle_mod, x)
+    for h in range(6):
+        kh = h % 2
+        qk = float(np.dot(x["q"][0, kh].astype(np.float64), x["k"][0, kh].astype(np.float64)))
+        ref = np.float64(x["beta"][0, h]) * qk * x["v"][0, h].astype(np.float64)
+        assert rel_err(o[0, h], ref) < 1e-14
+
+
+# --- P-d: zero gate with beta = 0 leaves the state unchanged -----------------------------
+
+def test_zero_gate_zero_beta_identity(oracle_mod):
+    x = _small(37, seed=7)
+    x["g"][:] = 0
+    x["beta"][:] = 0
+    o, s = _run(oracle_mod, x)
+    assert np.array_equal(s, x["s0"].astype(np.float64))
+    for h in range(6):
+        ref = x["q"][:, h % 2].astype(np.float64) @ x["s0"][h].astype(np.float64)
+        assert rel_err(o[:, h], ref) < 1e-14
+
+
+# --- P-e: write-read identity of the delta rule -------------------------------------------
+
+def test_write_read_identity(oracle_mod):
+    """After a token, S_t^T k_t = e^g (1 - beta |k|^2) S_{t-1}^T k_t + beta |k|^2 v_t."""
+    rng = np.random.default_rng(11)
+    dk, dv, T = 32, 24, 20
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk)) * 0.3
+    v = rng.standard_normal((T, dv))
+    g = -rng.uniform(0.01, 1.0, T)
+    beta = rng.uniform(0.05, 0.95, T)
+    S = rng.standard_normal((dk, dv)) * 0.1
+    for t in range(T):
+        _, S_new = oracle_mod.recurrence_f64(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1],
+                                             beta[t:t + 1], S)
+        kk = float(k[t] @ k[t])
+        ref = np.exp(g[t]) * (1 - beta[t] * kk) * (S.T @ k[t]) + beta[t] * kk * v[t]
+        assert rel_err(S_new.T @ k[t], ref) < 1e-13
+        S = S_new
+
+
+def test_write_read_unit_key(oracle_mod):
+    """With beta = 1 and a unit key the state maps k_t exactly onto v_t."""
+    rng = np.random.default_rng(12)
+    dk, dv = 128, 128
+    k = rng.standard_normal((1, dk))
+    k /= np.linalg.norm(k)
+    v = rng.standard_normal((1, dv))
+    S = rng.standard_normal((dk, dv)) * 0.1
+    _, S1 = oracle_mod.recurrence_f64(rng.standard_normal((1, dk)), k, v, np.array([-0.3]),
+                                      np.array([1.0]), S)
+    assert rel_err(S1.T @ k[0], v[0]) < 1e-13
+
+
+# --- P-f: reset (decay to ~0, beta = 1) -----------------------------------------------------
+
+def test_reset_forgets_initial_state(oracle_mod):
+    x = _small(6, seed=13)
+    x["g"][:] = -60.0
+    x["beta"][:] = 1.0
+    o, s = _run(oracle_mod, x)
+    for h in range(6):
+        kh = h % 2
+        kk = x["k"][:, kh].astype(np.float64)
+        qq = x["q"][:, kh].astype(np.float64)
+        vv = x["v"][:, h].astype(np.float64)
+        # what is left of the earlier state is e^-60 (~1e-26) times it: FP64 rounding only
+        assert rel_err(s[h], np.outer(kk[-1], vv[-1])) < 1e-14
+        ref_o = np.sum(qq * kk, axis=1)[:, None] * vv
+        assert rel_err(o[:, h], ref_o) < 1e-14
+
+
+# --- P-g: split invariance (state chaining) -------------------------------------------------
+
+def test_split_invariance(oracle_mod):
+    rng = np.random.default_rng(14)
+    dk, dv, T, T1 = 128, 128, 50, 21
+    q = rng.standard_normal((T, dk)) / 12
+    k = rng.standard_normal((T, dk)) / 12
+    v = rng.standard_normal((T, dv))
+    g = -np.exp(rng.uniform(-4, 0, T))
+    b = rng.uniform(0, 1, T)
+    S0 = rng.standard_normal((dk, dv)) * 0.1
+    o, S = oracle_mod.recurrence_f64(q, k, v, g, b, S0)
+    o1, Sm = oracle_mod.recurrence_f64(q[:T1], k[:T1], v[:T1], g[:T1], b[:T1], S0)
+    o2, S2 = oracle_mod.recurrence_f64(q[T1:], k[T1:], v[T1:], g[T1:], b[T1:], Sm)
+    assert np.array_equal(np.concatenate([o1, o2]), o)
+    assert np.array_equal(S2, S)
+
+
+# --- P-h: linearity in (S0, v) -----------------------------------------------------------------
+
+def test_linearity_in_state_and_value(oracle_mod):
+    rng = np.random.default_rng(15)
+    dk, dv, T = 64, 48, 30
+    q = rng.standard_normal((T, dk)) / 8
+    k = rng.standard_normal((T, dk)) / 8
+    v = rng.standard_normal((T, dv))
+    g = -np.exp(rng.uniform(-4, 0, T))
+    b = rng.uniform(0, 1, T)
+    S0 = rng.standard_normal((dk, dv)) * 0.1
+    o, S = oracle_mod.recurrence_f64(q, k, v, g, b, S0)
+    oa, Sa = oracle_mod.recurrence_f64(q, k, np.zeros_like(v), g, b, S0)
+    ob, Sb = oracle_mod.recurrence_f64(q, k, v, g, b, np.zeros_like(S0))
+    assert rel_err(oa + ob, o) < 1e-13
+    assert rel_err(Sa + Sb, S) < 1e-13
+    assert rel_err(oa, o) > 1e-3 and rel_err(ob, o) > 1e-3
+
+
+# --- P-i: head structure (value head h reads key head h mod Hk) ----------------------------
+
+def test_key_head_sharing(oracle_mod):
+    x = make_inputs(9, seed=16)
+    for name in ("v", "g", "beta"):
+        x[name][:, 16] = x[name][:, 0]
+        x[name][:, 32] = x[name][:, 0]
+        x[name][:, 1] = x[name][:, 0]
+    x["s0"][16] = x["s0"][0]
+    x["s0"][32] = x["s0"][0]
+    x["s0"][1] = x["s0"][0]
+    o, s = _run(oracle_mod, x)
+    assert np.array_equal(o[:, 16], o[:, 0]) and np.array_equal(o[:, 32], o[:, 0])
+    assert np.array_equal(s[16], s[0])
+    assert rel_err(o[:, 1], o[:, 0]) > 1e-3   # heads 0 and 1 read different key heads
+
+
+def test_heads_are_independent(oracle_mod):
+    x = make_inputs(7, seed=17)
+    o, s = _run(oracle_mod, x)
+    x2 = {kk: vv.copy() for kk, vv in x.items()}
+    x2["v"][:, 5] += 1.0
+    x2["g"][:, 5] *= 0.5
+    x2["beta"][:, 5] *= 0.5
+    o2, s2 = _run(oracle_mod, x2)
+    others = [h for h in range(48) if h != 5]
+    assert np.array_equal(o2[:, others], o[:, others])
+    assert np.array_equal(s2[others], s[others])
+    assert rel_err(o2[:, 5], o[:, 5]) > 1e-3
+
+
+def test_head_selection_matches_full_run(oracle_mod):
+    x = make_inputs(11, seed=18)
+    o, s = _run(oracle_mod, x)
+    sel = [47, 3, 20]
+    o_s, s_s = _run(oracle_mod, x, heads=sel)
+    assert np.array_equal(o_s, o[:, sel])
+    assert np.array_equal(s_s, s[sel])
+
+
+# --- P-j: norm bound (the update is a contraction for |k| <= 1, 0 <= beta <= 1) -----------
+
+def test_state_norm_bound(oracle_mod):
+    rng = np.random.default_rng(19)
+    dk, dv, T = 64, 64, 40
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    g = -np.exp(rng.uniform(-4, 0, T))
+    b = rng.uniform(0, 1, T)
+    S = rng.standard_normal((dk, dv))
+    for t in range(T):
+        _, Sn = oracle_mod.recurrence_f64(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1],
+                                          b[t:t + 1], S)
+        bound = np.exp(g[t]) * np.linalg.norm(S, 2) + b[t] * np.linalg.norm(v[t])
+        assert np.linalg.norm(Sn, 2) <= bound * (1 + 1e-12)
+        S = Sn
+
+
+# --- exact rational brute force on a tiny state ---------------------------------------------
+
+def test_exact_rational_tiny():
+    """dk = 3, dv = 2, decay exactly 1/2 (g = ln 1/2), dyadic inputs: the recurrence is
+    evaluated in exact rational arithmetic and compared with the oracle."""
+    import oracle
+    q = [[Fraction(1, 2), Fraction(-1, 4), Fraction(3, 8)],
+         [Fraction(0), Fraction(1, 2), Fraction(-1, 2)],
+         [Fraction(1, 8), Fraction(1, 8), Fraction(1, 4)]]
+    k = [[Fraction(1, 2), Fraction(1, 2), Fraction(0)],
+         [Fraction(-1, 4), Fraction(1, 2), Fraction(1, 4)],
+         [Fraction(3, 4), Fraction(0), Fraction(-1, 4)]]
+    v = [[Fraction(1), Fraction(-2)], [Fraction(1, 2), Fraction(3, 2)], [Fraction(-1), Fraction(1, 4)]]
+    beta = [Fraction(1, 2), Fraction(3, 4), Fraction(1, 4)]
+    a = Fraction(1, 2)
+    S = [[Fraction(1, 8), Fraction(0)], [Fraction(-1, 4), Fraction(1, 2)], [Fraction(0), Fraction(1, 16)]]
+    outs = []
+    for t in range(3):
+        # d_j = beta (v_j - a sum_i S_ij k_i);  S_ij <- a S_ij + k_i d_j;  o_j = sum_i S_ij q_i
+        d = [beta[t] * (v[t][j] - a * sum(S[i][j] * k[t][i] for i in range(3))) for j in range(2)]
+        S = [[a * S[i][j] + k[t][i] * d[j] for j in range(2)] for i in range(3)]
+        outs.append([sum(S[i][j] * q[t][i] for i in range(3)) for j in range(2)])
+    f = lambda m: np.array([[float(e) for e in row] for row in m])
+    S0 = np.array([[1 / 8, 0], [-1 / 4, 1 / 2], [0, 1 / 16]])
+    o, St = oracle.recurrence_f64(f(q), f(k), f(v), np.full(3, np.log(0.5)),
+                                  np.array([float(b) for b in beta]), S0)
+    np.testing.assert_allclose(o, f(outs), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(St, f(S), rtol=0, atol=1e-15)
+
+
+# --- O2: the gated RMS output norm ----------------------------------------------------------
+
+def test_norm_reduces_to_rms_norm(oracle_mod):
+    """w = 1 and a saturated gate (z = 40, sigmoid = 1 in FP64) give plain RMSNorm."""
+    import torch
+    rng = np.random.default_rng(20)
+    o = rng.standard_normal((5, 4, 128))
+    z = np.full_like(o, 40.0)
+    w = np.ones((4, 128))
+    eps = 1e-6
+    _, y64 = oracle_mod.out_norm(o, z, w, eps, return_prerounding=True)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(o), (128,), eps=eps).numpy()
+    assert rel_err(y64, ref) < 1e-15
+
+
+def test_norm_constant_row_and_gate(oracle_mod):
+    c, eps = 0.75, 1e-3
+    o = np.full((1, 1, 128), c)
+    z = np.linspace(-3, 3, 128).reshape(1, 1, 128)
+    w = (1 + np.arange(128) / 256.0).reshape(1, 128)
+    _, y64 = oracle_mod.out_norm(o, z, w, eps, return_prerounding=True)
+    ref = w[0] * (1 / (1 + np.exp(-z[0, 0]))) * c / np.sqrt(c * c + eps)
+    assert rel_err(y64[0, 0], ref) < 1e-15
+
+
+def test_norm_scale_invariance(oracle_mod):
+    rng = np.random.default_rng(21)
+    o = rng.standard_normal((3, 2, 128))
+    z = rng.standard_normal((3, 2, 128))
+    w = 1 + 0.1 * rng.standard_normal((2, 128))
+    _, y1 = oracle_mod.out_norm(o, z, w, 0.0, return_prerounding=True)
+    _, y2 = oracle_mod.out_norm(37.5 * o, z, w, 0.0, return_prerounding=True)
+    assert rel_err(y2, y1) < 1e-14
+
+
+def test_norm_uses_weight_of_own_head(oracle_mod):
+    rng = np.random.default_rng(22)
+    o = rng.standard_normal((2, 3, 128))
+    z = rng.standard_normal((2, 3, 128))
+    w = np.stack([np.full(128, 1.0), np.full(128, 2.0), np.full(128, 4.0)])
+    _, y = oracle_mod.out_norm(o, z, w, 1e-6, return_prerounding=True)
+    _, y1 = oracle_mod.out_norm(o, z, np.ones((3, 128)), 1e-6, return_prerounding=True)
+    np.testing.assert_allclose(y[:, 1], 2 * y1[:, 1], rtol=1e-15)
+    np.testing.assert_allclose(y[:, 2], 4 * y1[:, 2], rtol=1e-15)
+
+
+# --- P-l: binary16 round-to-nearest-even ------------------------------------------------------
+
+def test_f16_rounding_matches_numpy(oracle_mod):
+    rng = np.random.default_rng(23)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e6, -1e6, 6.1e-5, 5.96e-8,
+                  2.98e-8, 2.9802322387695312e-08, 2.98023223876953125e-08 * 1.0000001,
+                  1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5, 2.0 ** -24 * 2.5,
+                  np.inf, -np.inf]),
+    ])
+    ours = np.array([oracle_mod.f64_to_f16_bits(x) for x in vals], dtype=np.uint16)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert oracle_mod.f64_to_f16_bits(float("nan")) & 0x7c00 == 0x7c00
+
+
+def test_norm_output_is_rounded_prerounding(oracle_mod):
+    rng = np.random.default_rng(24)
+    o = rng.standard_normal((4, 3, 128))
+    z = rng.standard_normal((4, 3, 128))
+    w = 1 + 0.1 * rng.standard_normal((3, 128))
+    y, y64 = oracle_mod.out_norm(o, z, w, 1e-6, return_prerounding=True)
+    assert np.array_equal(y.view(np.uint16), y64.astype(np.float16).view(np.uint16))
