@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the prompt-path gated DeltaNet layer on one MI355X.
+
+Workload (one step): one layer at T = 32768 tokens, 16 key heads x 3 value heads (48),
+dk = dv = 128, seeded synthetic inputs already resident in HBM:
+  1. gdn_recurrence_chunked  (WY form, chunk 32, 16 super-blocks of 2048 tokens, the FP32
+                              state carried between them), then
+  2. gdn_out_norm            (gated RMS norm of the 48 x 128 outputs to FP16).
+Metric: microseconds per token per layer for the whole step (lower is better); the JSON
+line also carries the roofline of the dominant kernel (the chunk scan, timed live with
+HIP events recorded around each of its launches) and the FP64 CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/token/layer (48 v-heads, dk=dv=128) at T=32768; % FP32 roofline"
+FLOP_PER_TOKEN = 6 * 128 * 128 * 48          # kv sum, update and output sum per state element
+RECURRENCE_BYTES_PER_TOKEN = 4 * (2 * 16 * 128 + 2 * 48 + 2 * 48 * 128)   # q,k,g,beta,v in; o out
+NORM_BYTES_PER_TOKEN = 48 * 128 * (4 + 4 + 2)                              # o, z in; y out
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+SUPER_BLOCK = 2048
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so.7")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream_handle):
+        if self.L.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(f.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.L.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def traffic_from_profile():
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
+    taken on the current scan kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "chunk_scan_traffic.json")
+    src = os.path.join(ROOT, "linear_attention_recurrence_gated_amd", "csrc", "gdn_chunk.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(x, tokens):
+    """The FP64 oracle (recurrence + norm) on the first `tokens` tokens, all 48 heads."""
+    import oracle
+    sl = {n: (a[:tokens] if n in ("q", "k", "v", "g", "beta", "z") else a) for n, a in x.items()}
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    o, _ = oracle.recurrence(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["s0"],
+                             threads=threads)
+    oracle.out_norm(o, sl["z"], sl["w"], 1e-6, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": dt * 1e6 / tokens, "unit": "µs/token/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": "first %d of the 32768 tokens, all 48 value heads: FP64 recurrence + "
+                      "gated RMS norm (%.1f s wall)" % (tokens, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=32768)
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the CPU-oracle sample (0 disables the CPU baseline)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode (each box has "
+              "one GPU); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrence_gated_amd import gdn, make_inputs
+
+    T = args.tokens
+    dev = torch.device("cuda:0")
+    print("bench: generating inputs T=%d" % T, file=sys.stderr, flush=True)
+    x = make_inputs(T, seed=0, with_norm=True)
+    d = {n: torch.from_numpy(a).to(dev) for n, a in x.items()}
+    o = torch.empty_like(d["v"])
+    st = torch.empty_like(d["s0"])
+    y = torch.empty(d["v"].shape, dtype=torch.float16, device=dev)
+    ws = gdn.workspace(dev, 16, 48)
+    stream = torch.cuda.current_stream(dev)
+    hip = HipEvents()
+    nsb = (T + SUPER_BLOCK - 1) // SUPER_BLOCK
+
+    def step(scan_ev=None, norm_ev=None):
+        gdn.recurrence_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"],
+                               state_out=st, o=o, ws=ws, scan_events=scan_ev)
+        if norm_ev:
+            hip.record(norm_ev[0], stream.cuda_stream)
+        gdn.out_norm(o, d["z"], d["w"], eps=1e-6, y=y)
+        if norm_ev:
+            hip.record(norm_ev[1], stream.cuda_stream)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    scan_ev = [hip.create(2 * nsb) for _ in range(args.steps)]
+    norm_ev = [hip.create(2) for _ in range(args.steps)]
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(scan_ev[i], norm_ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    scan_ms = [hip.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for ev in scan_ev for j in range(nsb)]
+    norm_ms = [hip.elapsed_ms(ev[0], ev[1]) for ev in norm_ev]
+    for ev in scan_ev + norm_ev:
+        hip.destroy(ev)
+    full = T // SUPER_BLOCK  # scan launches over full super-blocks
+    scan_full_ms = [m for i, m in enumerate(scan_ms) if (i % nsb) < full] or scan_ms
+    scan_avg_ms = sum(scan_full_ms) / len(scan_full_ms)
+    norm_avg_ms = sum(norm_ms) / len(norm_ms)
+    flop_per_launch = FLOP_PER_TOKEN * min(SUPER_BLOCK, T)
+    achieved = flop_per_launch / (scan_avg_ms * 1e-3) / 1e12
+    y_ok = bool(torch.isfinite(y.float()).all().item()) and bool(torch.isfinite(st).all().item())
+
+    # the sequential kernel at the same size, for context (outside the timed region)
+    evs = hip.create(2)
+    gdn.recurrence_seq(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], state_out=st, o=o)
+    hip.record(evs[0], stream.cuda_stream)
+    gdn.recurrence_seq(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], state_out=st, o=o)
+    hip.record(evs[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    seq_ms = hip.elapsed_ms(evs[0], evs[1])
+    hip.destroy(evs)
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        print("bench: CPU oracle on %d tokens" % args.cpu_tokens, file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x, min(args.cpu_tokens, T))
+
+    traffic = traffic_from_profile()
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3 / T, 6),
+        "unit": "µs/token/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "one gated DeltaNet layer, T=%d, 16 key heads x 3 value heads, "
+                        "dk=dv=128: chunked WY recurrence (chunk 32, %d super-blocks of 2048 "
+                        "tokens, fp32 state carried) + gated RMS norm to fp16" % (T, nsb),
+            "T": T, "n_k_heads": 16, "n_v_heads": 48, "dk": 128, "dv": 128,
+            "chunk": 32, "super_block": SUPER_BLOCK, "seed": 0,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "chunk_scan_kernel",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+            "traffic": traffic,
+            "flop_per_launch": flop_per_launch,
+            "avg_launch_ms": round(scan_avg_ms, 5),
+            "launches_timed": len(scan_full_ms),
+        },
+        "breakdown": {
+            "scan_ms_per_step": round(sum(scan_ms) / args.steps, 4),
+            "norm_ms_per_step": round(norm_avg_ms, 4),
+            "norm_hbm_GBps": round(NORM_BYTES_PER_TOKEN * T / (norm_avg_ms * 1e-3) / 1e9, 1),
+            "norm_hbm_frac": round(NORM_BYTES_PER_TOKEN * T / (norm_avg_ms * 1e-3) / 1e9
+                                   / PEAK_HBM_GBS, 4),
+            "recurrence_us_per_token": round((ms_per_step - norm_avg_ms) * 1e3 / T, 6),
+            "seq_recurrence_us_per_token": round(seq_ms * 1e3 / T, 6),
+            "outputs_finite": y_ok,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

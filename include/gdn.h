@@ -1,0 +1,160 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated DeltaNet prompt-path library (libgdn.so).
+ *
+ * What the library computes, per value head h, for tokens t = 0 .. T-1, with a
+ * dk x dv FP32 state S (row i = key dim, column j = value dim):
+ *
+ *     S_t = e^{g_t} S_{t-1} + k_t ( beta_t ( v_t - e^{g_t} S_{t-1}^T k_t ) )^T
+ *     o_t = S_t^T q_t
+ *
+ * ("#413 prefill: DeltaNet recurrence with the three value heads of a key head in one
+ * thread", sections "What changes" and "Exactness": the kv sum, the delta, the state
+ * update and the output sum, evaluated one token at a time.)  Value head h reads key head
+ * h mod n_k_heads (same page, "What changes": the heads sharing a key head are h, h+16,
+ * h+32 for 16 key heads).  g is the log-decay (g <= 0; the decay factor is e^g).
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is a DEVICE pointer owned by the caller (the library never
+ *    allocates, frees or keeps a pointer across calls) and must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Each call
+ *    validates its arguments on the host, enqueues its kernels on `stream` and returns
+ *    without synchronising; results are ready after the caller synchronises the stream.
+ *    Kernel faults surface at that synchronisation, as for any HIP library.
+ *  - Arguments are validated before anything is enqueued: a rejected call returns a
+ *    non-zero gdn_status and changes no memory.  No C++ exception crosses the ABI and
+ *    the library prints nothing.
+ *  - Only dk = dv = 128 is supported; n_v_heads must be a positive multiple of
+ *    n_k_heads with at most 4 value heads per key head; T * n_v_heads * dv must be
+ *    below 2^31 (32-bit element offsets).
+ *    Anything else is GDN_ERR_BAD_SHAPE -- there is no fallback path.
+ *  - Layouts (row-major, contiguous, float32 unless stated):
+ *        q, k         [T][n_k_heads][dk]   (the library applies no normalisation/scale)
+ *        v, o         [T][n_v_heads][dv]
+ *        g, beta      [T][n_v_heads]
+ *        state_in/out [n_v_heads][dk][dv]
+ *        z            [T][n_v_heads][dv]   w [n_v_heads][dv]   y [T][n_v_heads][dv] fp16
+ *  - Calls on different streams must not share output buffers or a workspace.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                                  */
+  GDN_ERR_BAD_SHAPE = 2,    /* T < 0, dk/dv != 128, heads < 1, n_v_heads % n_k_heads != 0,
+                               n_v_heads / n_k_heads > 4, T * n_v_heads * dv >= 2^31, or
+                               a negative / non-finite eps                                 */
+  GDN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned                            */
+  GDN_ERR_ALIASING = 4,     /* an output overlaps an input or another output
+                               (state_out == state_in exactly is allowed)                  */
+  GDN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than gdn_chunked_workspace_bytes() */
+  GDN_ERR_HIP = 6           /* a HIP runtime call or a launch failed: gdn_last_hip_error()  */
+};
+
+/*
+ * Sequential recurrence: walks the tokens one at a time ("#413 ...", sections "What
+ * changes" and "Exactness"; the order within a token is kv sum, delta, update, output).
+ *
+ *   q, k, v, g, beta : inputs (layouts above), read only.
+ *   state_in         : S_0 per value head, read only (may equal state_out).
+ *   state_out        : S_T per value head, written.  state_out == state_in is allowed
+ *                      (in-place); any other overlap with an input is GDN_ERR_ALIASING.
+ *   o                : o_t per token and value head, written.
+ *   T = 0            : nothing is written to o; state_in is copied to state_out if they
+ *                      differ; returns GDN_OK (o may then be NULL).
+ */
+int gdn_recurrence_seq(const float* q, const float* k, const float* v, const float* g,
+                       const float* beta, const float* state_in, float* state_out, float* o,
+                       int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* stream);
+
+/*
+ * Bytes of caller-owned device scratch that gdn_recurrence_chunked needs.  It does not
+ * depend on T: the scratch holds the per-chunk operators of one 2048-token super-block
+ * ("#1372 DeltaNet recurrence: STRATA_GDN_CHUNKED=1", section "What it does", paragraph
+ * "Scratch": the prep output of one super-block, allocated once per device and kept).
+ * Returns 0 for an unsupported shape.
+ */
+size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv);
+
+/*
+ * Chunked recurrence in the WY form ("#1372 ...", section "What it does"): the same
+ * function as gdn_recurrence_seq, computed in chunks of 32 tokens.  Per chunk and value
+ * head, with gamma the inclusive running sum of g inside the chunk and S0 the state
+ * before it:
+ *     A[t][i] = beta_t e^{gamma_t - gamma_i} k_t.k_i   (i < t),   T = (I + A)^-1,
+ *     D = T beta (V - e^{gamma} K S0),
+ *     O = e^{gamma} Q S0 + P D,  P[t][i] = e^{gamma_t - gamma_i} q_t.k_i  (i <= t),
+ *     S' = e^{gamma_last} S0 + K^T e^{gamma_last - gamma} D.
+ * A prep kernel forms the chunk operators for every chunk of a 2048-token super-block at
+ * once; a scan kernel then walks the super-block's chunks carrying the state on chip.
+ * The state passes between super-blocks through state_out.  A last partial chunk is
+ * padded with zero tokens (g = 0, beta = 0), which leave the state unchanged.
+ *
+ *   workspace, workspace_bytes : device scratch of at least
+ *                      gdn_chunked_workspace_bytes(...) bytes, 16-byte aligned.  Its
+ *                      contents on entry do not matter and on return are unspecified.
+ *                      It must not overlap any input or output.
+ *   Other arguments, aliasing rules and T = 0 behave as for gdn_recurrence_seq.
+ *   Results differ from gdn_recurrence_seq only by float32 summation order.
+ */
+int gdn_recurrence_chunked(const float* q, const float* k, const float* v, const float* g,
+                           const float* beta, const float* state_in, float* state_out,
+                           float* o, int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling variant of gdn_recurrence_chunked: the same validation and the same work on
+ * the same stream; in addition it records the caller's events scan_events[2i] and
+ * scan_events[2i+1] (hipEvent_t values, created by the caller) on `stream` immediately
+ * before and after the scan kernel of super-block i, for every i with 2i+1 <
+ * n_scan_events.  This lets a caller time the scan kernel alone without a profiler.
+ * scan_events may be NULL only when n_scan_events <= 0 (then this is
+ * gdn_recurrence_chunked exactly).
+ */
+int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
+                                 const float* g, const float* beta, const float* state_in,
+                                 float* state_out, float* o, int64_t T, int n_k_heads,
+                                 int n_v_heads, int dk, int dv, void* workspace,
+                                 size_t workspace_bytes, void* const* scan_events,
+                                 int n_scan_events, void* stream);
+
+/*
+ * Gated RMS output norm to FP16 ("#413 ...", section "What changes": the output norm
+ * reads the FP32 recurrence output and writes only the FP16 copy y_h that the out
+ * projection reads; the pages print no formula, and the library takes the plain reading
+ * of a gated RMS norm with a per-value-head weight and a sigmoid gate):
+ *
+ *   y[t][h][j] = fp16_rne( o[t][h][j] * rsqrt(mean_j o[t][h][:]^2 + eps)
+ *                          * w[h][j] * sigmoid(z[t][h][j]) )
+ *
+ *   o, z, w : inputs (layouts above), read only.  eps >= 0 (a negative or non-finite eps
+ *             is GDN_ERR_BAD_SHAPE).
+ *   y       : output, IEEE binary16 bit patterns, rounded to nearest even.  Must not
+ *             overlap o, z or w.
+ *   T = 0   : nothing is written; returns GDN_OK.
+ */
+int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint16_t* y,
+                 int64_t T, int n_v_heads, int dv, void* stream);
+
+/* A static, never-NULL description of a gdn_status value. */
+const char* gdn_status_string(int status);
+
+/* The hipError_t of the most recent GDN_ERR_HIP returned on the calling thread
+   (0 if none). */
+int gdn_last_hip_error(void);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

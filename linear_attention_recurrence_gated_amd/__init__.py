@@ -14,6 +14,6 @@ __all__ = ["make_inputs", "EDGE_LENGTHS", "N_K_HEADS", "N_V_HEADS", "DK", "DV", 
 
 def __getattr__(name):
     if name == "gdn":
-        from . import gdn as _gdn
-        return _gdn
+        import importlib
+        return importlib.import_module(__name__ + ".gdn")
     raise AttributeError(name)

@@ -1,0 +1,209 @@
+// C ABI of libgdn (declared in include/gdn.h): host-side validation, then kernel launches
+// on the caller's stream.  Validation happens before any HIP call, so a rejected call
+// touches neither memory nor the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "gdn.h"
+#include "gdn_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return GDN_ERR_HIP;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int64_t T, int n_k_heads, int n_v_heads, int dk, int dv) {
+  if (T < 0 || n_k_heads < 1 || n_v_heads < 1) return GDN_ERR_BAD_SHAPE;
+  if (dk != gdn::kDim || dv != gdn::kDim) return GDN_ERR_BAD_SHAPE;
+  if (n_v_heads % n_k_heads != 0) return GDN_ERR_BAD_SHAPE;
+  if (n_v_heads / n_k_heads > gdn::kMaxGroup) return GDN_ERR_BAD_SHAPE;
+  if (T * (int64_t)n_v_heads * dv >= ((int64_t)1 << 31)) return GDN_ERR_BAD_SHAPE;
+  return GDN_OK;
+}
+
+// Shared validation of the two recurrence entry points.
+int check_recurrence(const float* q, const float* k, const float* v, const float* g,
+                     const float* beta, const float* state_in, const float* state_out,
+                     const float* o, int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                     const void* workspace, size_t ws_bytes, bool chunked) {
+  if (int s = check_shape(T, n_k_heads, n_v_heads, dk, dv)) return s;
+  if (!state_in || !state_out) return GDN_ERR_NULL_POINTER;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  if (chunked && T > 0 && !workspace) return GDN_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, g, beta, state_in, state_out, o, chunked ? workspace : nullptr};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+  if (chunked && T > 0 &&
+      ws_bytes < gdn_chunked_workspace_bytes(n_k_heads, n_v_heads, dk, dv))
+    return GDN_ERR_WORKSPACE;
+
+  const size_t f = sizeof(float);
+  const size_t qk_b = (size_t)T * n_k_heads * dk * f, v_b = (size_t)T * n_v_heads * dv * f;
+  const size_t gb_b = (size_t)T * n_v_heads * f, s_b = (size_t)n_v_heads * dk * dv * f;
+  const Range in[] = {range_of(q, q ? qk_b : 0), range_of(k, k ? qk_b : 0),
+                      range_of(v, v ? v_b : 0),  range_of(g, g ? gb_b : 0),
+                      range_of(beta, beta ? gb_b : 0), range_of(state_in, s_b)};
+  const Range r_o = range_of(o, o ? v_b : 0), r_s = range_of(state_out, s_b);
+  for (const Range& r : in)
+    if (overlap(r_o, r)) return GDN_ERR_ALIASING;
+  for (int i = 0; i < 5; ++i)  // q, k, v, g, beta
+    if (overlap(r_s, in[i])) return GDN_ERR_ALIASING;
+  // state_out may be state_in itself (in place) but must not partly overlap it
+  if (state_out != state_in && overlap(r_s, in[5])) return GDN_ERR_ALIASING;
+  if (overlap(r_o, r_s)) return GDN_ERR_ALIASING;
+  if (chunked && T > 0) {
+    const Range r_w = range_of(workspace, ws_bytes);
+    for (const Range& r : in)
+      if (overlap(r_w, r)) return GDN_ERR_ALIASING;
+    if (overlap(r_w, r_o) || overlap(r_w, r_s)) return GDN_ERR_ALIASING;
+  }
+  return GDN_OK;
+}
+
+int copy_state_if_needed(const float* state_in, float* state_out, int n_v_heads, int dk,
+                         int dv, hipStream_t s) {
+  if (state_out == state_in) return GDN_OK;
+  const hipError_t e = hipMemcpyAsync(state_out, state_in,
+                                      (size_t)n_v_heads * dk * dv * sizeof(float),
+                                      hipMemcpyDeviceToDevice, s);
+  return e == hipSuccess ? GDN_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_recurrence_seq(const float* q, const float* k, const float* v, const float* g,
+                       const float* beta, const float* state_in, float* state_out, float* o,
+                       int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* stream) {
+  if (int st = check_recurrence(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads,
+                                n_v_heads, dk, dv, nullptr, 0, false))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return copy_state_if_needed(state_in, state_out, n_v_heads, dk, dv, s);
+  gdn::SeqArgs a{q, k, v, g, beta, state_in, state_out, o, (int)T, n_k_heads};
+  const hipError_t e = gdn::launch_seq(a, n_v_heads / n_k_heads, s);
+  return e == hipSuccess ? GDN_OK : hip_fail(e);
+}
+
+size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv) {
+  if (check_shape(0, n_k_heads, n_v_heads, dk, dv) != GDN_OK) return 0;
+  return (size_t)gdn::kChunksPerSB * n_v_heads * gdn::kSlot * sizeof(float);
+}
+
+}  // extern "C"
+
+namespace {
+
+int chunked_impl(const float* q, const float* k, const float* v, const float* g,
+                 const float* beta, const float* state_in, float* state_out, float* o,
+                 int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* workspace,
+                 size_t workspace_bytes, void* const* scan_events, int n_scan_events,
+                 void* stream) {
+  if (int st = check_recurrence(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads,
+                                n_v_heads, dk, dv, workspace, workspace_bytes, true))
+    return st;
+  if (n_scan_events > 0 && !scan_events) return GDN_ERR_NULL_POINTER;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return copy_state_if_needed(state_in, state_out, n_v_heads, dk, dv, s);
+  int sb = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += gdn::kSuperBlock, ++sb) {
+    const int n = (int)((T - t0) < gdn::kSuperBlock ? (T - t0) : gdn::kSuperBlock);
+    gdn::ChunkArgs a{q, k, v, g, beta, t0 == 0 ? state_in : state_out, state_out, o,
+                     static_cast<float*>(workspace), (int)t0, n, n_k_heads, n_v_heads};
+    hipError_t e = gdn::launch_chunk_prep(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+    const bool timed = 2 * sb + 1 < n_scan_events;
+    if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(scan_events[2 * sb]), s)) !=
+                     hipSuccess)
+      return hip_fail(e);
+    e = gdn::launch_chunk_scan(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(scan_events[2 * sb + 1]), s)) !=
+                     hipSuccess)
+      return hip_fail(e);
+  }
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_recurrence_chunked(const float* q, const float* k, const float* v, const float* g,
+                           const float* beta, const float* state_in, float* state_out,
+                           float* o, int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
+                      dv, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
+                                 const float* g, const float* beta, const float* state_in,
+                                 float* state_out, float* o, int64_t T, int n_k_heads,
+                                 int n_v_heads, int dk, int dv, void* workspace,
+                                 size_t workspace_bytes, void* const* scan_events,
+                                 int n_scan_events, void* stream) {
+  return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
+                      dv, workspace, workspace_bytes, scan_events, n_scan_events, stream);
+}
+
+int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint16_t* y,
+                 int64_t T, int n_v_heads, int dv, void* stream) {
+  if (T < 0 || n_v_heads < 1 || dv != gdn::kDim) return GDN_ERR_BAD_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GDN_ERR_BAD_SHAPE;
+  if (T * (int64_t)n_v_heads * dv >= ((int64_t)1 << 31)) return GDN_ERR_BAD_SHAPE;
+  if (!w) return GDN_ERR_NULL_POINTER;
+  if (T > 0 && (!o || !z || !y)) return GDN_ERR_NULL_POINTER;
+  const void* ptrs[] = {o, z, w, y};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+  if (T == 0) return GDN_OK;
+  const size_t n = (size_t)T * n_v_heads * dv;
+  const Range r_y = range_of(y, n * sizeof(uint16_t));
+  if (overlap(r_y, range_of(o, n * sizeof(float))) ||
+      overlap(r_y, range_of(z, n * sizeof(float))) ||
+      overlap(r_y, range_of(w, (size_t)n_v_heads * dv * sizeof(float))))
+    return GDN_ERR_ALIASING;
+  gdn::NormArgs a{o, z, w, y, eps, (int)(T * n_v_heads), n_v_heads};
+  const hipError_t e = gdn::launch_out_norm(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : hip_fail(e);
+}
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "unsupported shape or argument value";
+    case GDN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case GDN_ERR_ALIASING: return "an output overlaps an input or another output";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gdn_last_hip_error(void) { return g_last_hip_error; }
+
+int gdn_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Device helpers shared by the gfx950 kernels of libgdn: wave64 cross-lane sums, the
+// FP32 matrix-core product and the XCD-aware block order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// DPP move within a row of 16 lanes (gfx9 DPP16 control codes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int DPP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within each 8 lanes
+constexpr int DPP_MIRROR = 0x140;       // lane i <- lane 15-i within each 16 lanes
+
+// Sum over the 32 lanes of each half of the wave; every lane receives its half's sum.
+// Four DPP steps reduce inside a row of 16 lanes, then v_permlane16_swap exchanges the
+// two rows of each half (rows 0<->1 and 2<->3), so both rows hold the 32-lane total.
+// Must be executed by all 32 lanes of the half.
+__device__ __forceinline__ float half_wave_sum(float x) {
+  x += dpp_mov<DPP_XOR1>(x);
+  x += dpp_mov<DPP_XOR2>(x);
+  x += dpp_mov<DPP_HALF_MIRROR>(x);
+  x += dpp_mov<DPP_MIRROR>(x);
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+}
+
+// D = A * B + C on a 16x16 tile with a K-step of 4 (v_mfma_f32_16x16x4_f32).
+// Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; the accumulator holds
+// C[4 * (l / 16) + r][l % 16] in register r.
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).  This
+// maps a workgroup id to a logical block so that consecutive logical blocks share an XCD
+// (and its L2): XCD x receives the logical range [x*n/8, (x+1)*n/8).
+__device__ __forceinline__ int xcd_grouped_block(int b, int n) {
+  return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+}
+
+}  // namespace gdn

@@ -1,0 +1,168 @@
+"""Thin Python binding of libgdn.so (include/gdn.h) over torch tensors.
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels; torch provides device memory and the current stream.  If the library has not
+been built, every call raises -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
+          3: "GDN_ERR_MISALIGNED", 4: "GDN_ERR_ALIASING", 5: "GDN_ERR_WORKSPACE",
+          6: "GDN_ERR_HIP"}
+
+# Names and C signatures of every exported entry point (mirrors include/gdn.h).
+_P, _I, _I64, _SZ, _F = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                         ctypes.c_float)
+SIGNATURES = {
+    "gdn_recurrence_seq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _P]),
+    "gdn_chunked_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "gdn_recurrence_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _P,
+                                    _SZ, _P]),
+    "gdn_recurrence_chunked_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
+                                          _P, _SZ, _P, _I, _P]),
+    "gdn_out_norm": (_I, [_P, _P, _P, _F, _P, _I64, _I, _I, _P]),
+    "gdn_status_string": (ctypes.c_char_p, [_I]),
+    "gdn_last_hip_error": (_I, []),
+    "gdn_abi_version": (_I, []),
+}
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        detail = lib().gdn_status_string(status).decode()
+        if status == 6:
+            detail += " (hipError_t %d)" % lib().gdn_last_hip_error()
+        super().__init__("%s failed: %s (%s)" % (fn, name, detail))
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build() or "
+                               "python -m linear_attention_recurrence_gated_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise GdnError(fn, status)
+
+
+def _f32(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous float32 tensor" % name)
+    return t
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _shapes(q, v):
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    return T, Hk, Hv, dk, dv
+
+
+def recurrence_seq(q, k, v, g, beta, state_in, state_out=None, o=None, stream=None):
+    """Sequential kernel.  Returns (o, state_out); state_out may be state_in (in place)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in")):
+        _f32(t, n)
+    T, Hk, Hv, dk, dv = _shapes(q, v)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    if o is None:
+        o = torch.empty_like(v)
+    _f32(state_out, "state_out"); _f32(o, "o")
+    st = lib().gdn_recurrence_seq(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(state_in), _ptr(state_out), _ptr(o), T, Hk, Hv, dk, dv,
+                                  _stream(stream, q.device))
+    _check("gdn_recurrence_seq", st)
+    return o, state_out
+
+
+def chunked_workspace_bytes(n_k_heads, n_v_heads, dk=128, dv=128):
+    return int(lib().gdn_chunked_workspace_bytes(n_k_heads, n_v_heads, dk, dv))
+
+
+_workspaces = {}
+
+
+def workspace(device, n_k_heads, n_v_heads, dk=128, dv=128):
+    """The chunked kernels' scratch: allocated once per device on first use and kept."""
+    need = chunked_workspace_bytes(n_k_heads, n_v_heads, dk, dv)
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def recurrence_chunked(q, k, v, g, beta, state_in, state_out=None, o=None, ws=None,
+                       stream=None, scan_events=None):
+    """Chunked WY kernels.  Returns (o, state_out).  ``scan_events`` (a sequence of raw
+    hipEvent_t handles) selects the profiling entry point, which records them around each
+    super-block's scan kernel."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in")):
+        _f32(t, n)
+    T, Hk, Hv, dk, dv = _shapes(q, v)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    if o is None:
+        o = torch.empty_like(v)
+    _f32(state_out, "state_out"); _f32(o, "o")
+    if ws is None:
+        ws = workspace(q.device, Hk, Hv, dk, dv)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out),
+            _ptr(o), T, Hk, Hv, dk, dv, _ptr(ws), ws.numel() * ws.element_size())
+    if scan_events is None:
+        st = lib().gdn_recurrence_chunked(*args, _stream(stream, q.device))
+        _check("gdn_recurrence_chunked", st)
+    else:
+        arr = (ctypes.c_void_p * max(1, len(scan_events)))(*scan_events)
+        st = lib().gdn_recurrence_chunked_timed(*args, arr, len(scan_events),
+                                                _stream(stream, q.device))
+        _check("gdn_recurrence_chunked_timed", st)
+    return o, state_out
+
+
+def out_norm(o, z, w, eps=1e-6, y=None, stream=None):
+    """Gated RMS output norm.  Returns y as a float16 tensor [T][Hv][dv]."""
+    _f32(o, "o"); _f32(z, "z"); _f32(w, "w")
+    T, Hv, dv = o.shape
+    if y is None:
+        y = torch.empty(o.shape, dtype=torch.float16, device=o.device)
+    if y.dtype != torch.float16 or not y.is_contiguous() or not y.is_cuda:
+        raise TypeError("y must be a contiguous float16 CUDA tensor")
+    st = lib().gdn_out_norm(_ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(y), T, Hv, dv,
+                            _stream(stream, o.device))
+    _check("gdn_out_norm", st)
+    return y

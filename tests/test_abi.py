@@ -1,0 +1,134 @@
+"""The C-ABI library (CPU only: no compute call reaches the device).
+
+Checks that libgdn.so loads, exports every function include/gdn.h declares, and that the
+host-side argument validation returns the documented status codes before any HIP call
+(every call here is rejected by validation, or is the T = 0 in-place no-op).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_gated_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULLP, SHAPE, MISAL, ALIAS, WS = 0, 1, 2, 3, 4, 5
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_recurrence_gated_amd import build
+        build.build()
+    return gdn.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in gdn.SIGNATURES, "binding lacks a signature for %s" % n
+
+
+def test_status_strings_and_version(L):
+    for s in range(0, 8):
+        assert L.gdn_status_string(s)
+    assert L.gdn_abi_version() == 1
+    assert L.gdn_last_hip_error() == 0
+
+
+def test_workspace_size(L):
+    assert L.gdn_chunked_workspace_bytes(16, 48, 128, 128) == 64 * 48 * 2176 * 4
+    assert L.gdn_chunked_workspace_bytes(16, 48, 64, 128) == 0
+    assert L.gdn_chunked_workspace_bytes(16, 40, 128, 128) == 0
+    assert L.gdn_chunked_workspace_bytes(1, 5, 128, 128) == 0   # at most 4 value heads per key head
+
+
+# Fake, never-dereferenced device addresses (validation rejects before any access).
+BASE = 0x7f0000000000
+MB = 1 << 20
+
+
+def _addrs(T=64, Hk=16, Hv=48):
+    qk = T * Hk * 128 * 4
+    vv = T * Hv * 128 * 4
+    gb = T * Hv * 4
+    st = Hv * 128 * 128 * 4
+    a = {}
+    cur = BASE
+    for name, size in (("q", qk), ("k", qk), ("v", vv), ("g", gb), ("beta", gb),
+                       ("s_in", st), ("s_out", st), ("o", vv), ("ws", 64 * Hv * 2176 * 4)):
+        a[name] = cur
+        cur += (size + MB) & ~(MB - 1)
+    return a
+
+
+def _seq(L, a, T=64, Hk=16, Hv=48, dk=128, dv=128):
+    P = ctypes.c_void_p
+    return L.gdn_recurrence_seq(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                                P(a["s_in"]), P(a["s_out"]), P(a["o"]), T, Hk, Hv, dk, dv, None)
+
+
+def _chunked(L, a, T=64, Hk=16, Hv=48, ws_bytes=None):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = L.gdn_chunked_workspace_bytes(Hk, Hv, 128, 128)
+    return L.gdn_recurrence_chunked(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                                    P(a["s_in"]), P(a["s_out"]), P(a["o"]), T, Hk, Hv, 128, 128,
+                                    P(a["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", [_seq, _chunked])
+def test_recurrence_validation(L, fn):
+    a = _addrs()
+    assert fn(L, dict(a, q=0)) == NULLP
+    assert fn(L, dict(a, s_out=0)) == NULLP
+    assert fn(L, a, T=-1) == SHAPE
+    assert fn(L, a, Hv=40) == SHAPE
+    assert fn(L, a, Hk=8, Hv=48) == SHAPE                       # 6 value heads per key head
+    assert fn(L, a, T=(1 << 31) // (48 * 128) + 1) == SHAPE     # 32-bit element offsets
+    assert fn(L, dict(a, v=a["v"] + 4)) == MISAL
+    assert fn(L, dict(a, o=a["q"])) == ALIAS                    # output over an input
+    assert fn(L, dict(a, s_out=a["v"])) == ALIAS
+    assert fn(L, dict(a, s_out=a["s_in"] + 1024)) == ALIAS      # partial overlap of the state
+    assert fn(L, dict(a, o=a["s_out"])) == ALIAS
+    # T = 0 in place: nothing to do, no device call
+    assert fn(L, dict(a, s_out=a["s_in"]), T=0) == OK
+
+
+def test_seq_dims(L):
+    a = _addrs()
+    assert _seq(L, a, dk=64) == SHAPE
+    assert _seq(L, a, dv=256) == SHAPE
+
+
+def test_chunked_workspace_validation(L):
+    a = _addrs()
+    assert _chunked(L, a, ws_bytes=1024) == WS
+    assert _chunked(L, dict(a, ws=0)) == WS
+    assert _chunked(L, dict(a, ws=a["ws"] + 8)) == MISAL
+    assert _chunked(L, dict(a, ws=a["v"])) == ALIAS
+
+
+def test_out_norm_validation(L):
+    P = ctypes.c_void_p
+    T, Hv = 64, 48
+    o, z, w, y = BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 192 * MB
+    f = L.gdn_out_norm
+    assert f(P(o), P(z), P(w), 1e-6, P(y), T, Hv, 64, None) == SHAPE
+    assert f(P(o), P(z), P(w), -1.0, P(y), T, Hv, 128, None) == SHAPE
+    assert f(P(o), P(z), P(w), float("nan"), P(y), T, Hv, 128, None) == SHAPE
+    assert f(P(o), P(z), P(w), 1e-6, P(y), -1, Hv, 128, None) == SHAPE
+    assert f(P(0), P(z), P(w), 1e-6, P(y), T, Hv, 128, None) == NULLP
+    assert f(P(o), P(z), P(0), 1e-6, P(y), T, Hv, 128, None) == NULLP
+    assert f(P(o), P(z), P(w), 1e-6, P(y + 2), T, Hv, 128, None) == MISAL
+    assert f(P(o), P(z), P(w), 1e-6, P(o + 256), T, Hv, 128, None) == ALIAS
+    assert f(P(o), P(z), P(w), 1e-6, P(y), 0, Hv, 128, None) == OK   # nothing to do

@@ -1,0 +1,198 @@
+"""Parity of the HIP path (through the C ABI) with the FP64 oracle, on the GPU.
+
+Gates (max|diff| / max|value| per tensor and call, against the oracle): 2e-6 for the
+sequential kernel, 5e-6 for the chunked kernels, for the outputs and the final state; the
+FP16 norm output within 1 unit in the last place.  Inputs are the seeded synthetic
+workloads of the pages' parity test: T = 64, the edge-length sweep from a non-zero state,
+T = 8192 with the output norm, T = 32768 chunked, and a 36-layer stack at T = 2048.
+"""
+import numpy as np
+import pytest
+
+from conftest import rel_err
+from gpu_util import CHUNKED_TOL, SEQ_TOL, f16_ulp_distance, log, run, to_dev
+from linear_attention_recurrence_gated_amd.inputs import EDGE_LENGTHS, make_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"seq": SEQ_TOL, "chunked": CHUNKED_TOL}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_recurrence_gated_amd import gdn
+    gdn.lib()  # raises if the library is not built: no fallback
+
+
+def _nan_like(t):
+    return torch.full_like(t, float("nan"))
+
+
+def _check(kind, x, d, heads=None, tag=""):
+    """Run `kind` with NaN-filled outputs (and workspace), compare with the oracle."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    ws = None
+    if kind == "chunked":
+        ws = gdn.workspace(d["q"].device, x["q"].shape[1], x["v"].shape[1])
+        ws.view(torch.float32).fill_(float("nan"))
+    log("run %s %s T=%d" % (kind, tag, x["q"].shape[0]))
+    o, s = run(kind, d, state_out=_nan_like(d["s0"]), o=_nan_like(d["v"]), ws=ws)
+    torch.cuda.synchronize()
+    o_h, s_h = o.cpu().numpy(), s.cpu().numpy()
+    assert not np.isnan(o_h).any() and not np.isnan(s_h).any()
+    sel = list(range(x["v"].shape[1])) if heads is None else list(heads)
+    o_ref, s_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"],
+                                     heads=sel)
+    eo, es = rel_err(o_h[:, sel], o_ref), rel_err(s_h[sel], s_ref)
+    log("  %s %s: out %.3e  state %.3e" % (kind, tag, eo, es))
+    assert eo <= TOL[kind], eo
+    assert es <= TOL[kind], es
+    return o, s, o_ref, s_ref
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_t64(kind):
+    x = make_inputs(64, seed=0)
+    _check(kind, x, to_dev(x), tag="T64")
+
+
+@pytest.mark.parametrize("T", EDGE_LENGTHS)
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_edge_lengths(kind, T):
+    x = make_inputs(T, seed=0)
+    _check(kind, x, to_dev(x), tag="edge")
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_rerun_bitwise(kind):
+    """Reruns give identical bits; for the chunked path the workspace is NaN-filled before
+    every other run (nothing reads scratch the prep has not written)."""
+    from linear_attention_recurrence_gated_amd import gdn
+    for T in (130, 2049, 4099):
+        x = make_inputs(T, seed=7)
+        d = to_dev(x)
+        ws = gdn.workspace(d["q"].device, 16, 48) if kind == "chunked" else None
+        log("rerun %s T=%d" % (kind, T))
+        ref = None
+        for i in range(6):
+            if ws is not None and i % 2 == 0:
+                ws.view(torch.float32).fill_(float("nan"))
+            o, s = run(kind, d, state_out=_nan_like(d["s0"]), o=_nan_like(d["v"]), ws=ws)
+            torch.cuda.synchronize()
+            cur = (o.cpu().numpy().view(np.uint32), s.cpu().numpy().view(np.uint32))
+            if ref is None:
+                ref = cur
+            else:
+                assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_in_place_state_and_split(kind):
+    """state_out == state_in works, and two calls T1 + T2 chained through the state match
+    the oracle over T1 + T2 (the state is the checkpoint between calls)."""
+    import oracle
+    T1, T2 = 2100, 1333
+    x = make_inputs(T1 + T2, seed=11)
+    d = to_dev(x)
+    st = d["s0"].clone()
+    parts = []
+    for a, b in ((0, T1), (T1, T1 + T2)):
+        dd = {n: d[n][a:b].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        dd["s0"] = st
+        log("split %s [%d,%d)" % (kind, a, b))
+        o, s = run(kind, dd, state_out=st)
+        assert s.data_ptr() == st.data_ptr()
+        parts.append(o)
+    torch.cuda.synchronize()
+    o = torch.cat(parts).cpu().numpy()
+    o_ref, s_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    assert rel_err(o, o_ref) <= TOL[kind]
+    assert rel_err(st.cpu().numpy(), s_ref) <= TOL[kind]
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_zero_tokens_copies_state(kind):
+    x = make_inputs(4, seed=1)
+    d = to_dev(x)
+    d = {n: (t[:0].contiguous() if n in ("q", "k", "v", "g", "beta") else t) for n, t in d.items()}
+    out = _nan_like(d["s0"])
+    o, s = run(kind, d, state_out=out, o=torch.empty_like(d["v"]))
+    torch.cuda.synchronize()
+    assert torch.equal(s, d["s0"])
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_zero_gate_zero_beta(kind):
+    """g = 0, beta = 0 leaves the state unchanged; outputs are S0^T q."""
+    x = make_inputs(77, seed=2)
+    x["g"][:] = 0
+    x["beta"][:] = 0
+    _, s, _, _ = _check(kind, x, to_dev(x), tag="identity")
+    assert rel_err(s.cpu().numpy(), x["s0"]) <= TOL[kind]
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_other_group_sizes(kind):
+    """1, 2 and 4 value heads per key head (the map h -> h mod n_k_heads)."""
+    for hk, hv in ((4, 4), (8, 16), (2, 8)):
+        x = make_inputs(100, seed=hv, n_k_heads=hk, n_v_heads=hv)
+        _check(kind, x, to_dev(x), tag="Hk%d/Hv%d" % (hk, hv))
+
+
+def test_t8192_seq_and_norm():
+    """One layer, T = 8192: sequential recurrence, then the gated RMS norm to FP16."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    x = make_inputs(8192, seed=0, with_norm=True)
+    d = to_dev(x)
+    o, s, o_ref, _ = _check("seq", x, d, tag="T8192")
+    log("norm T=8192")
+    y = gdn.out_norm(o, d["z"], d["w"], eps=1e-6, y=torch.full(o.shape, float("nan"),
+                                                               dtype=torch.float16,
+                                                               device=o.device))
+    torch.cuda.synchronize()
+    y_h = y.cpu().numpy()
+    # isolated: the oracle norm of the GPU's own FP32 output
+    y_iso = oracle.out_norm(o.cpu().numpy(), x["z"], x["w"], 1e-6)
+    dist = f16_ulp_distance(y_h, y_iso)
+    log("  norm isolated: max ulp %d, exact %.4f" % (dist.max(), (dist == 0).mean()))
+    assert dist.max() <= 1
+    # end to end: the oracle norm of the oracle's FP64 recurrence output
+    y_e2e = oracle.out_norm(o_ref, x["z"], x["w"], 1e-6)
+    dist = f16_ulp_distance(y_h, y_e2e)
+    log("  norm end-to-end: max ulp %d, exact %.4f" % (dist.max(), (dist == 0).mean()))
+    assert dist.max() <= 1
+
+
+def test_t32768_chunked_and_seq():
+    """One layer, T = 32768: 16 super-blocks of 2048 tokens in one chunked call, the state
+    carried between them; the sequential kernel beside it.  Six value heads are checked
+    against the oracle over the whole sequence (both members of two key-head groups and
+    heads from each column block of the scan)."""
+    x = make_inputs(32768, seed=0)
+    d = to_dev(x)
+    heads = [0, 16, 32, 5, 21, 47]
+    _check("chunked", x, d, heads=heads, tag="T32768")
+    _check("seq", x, d, heads=heads, tag="T32768")
+
+
+def test_36_layer_stack():
+    """36 independent layers (seed = layer), T = 2048 each: chunked recurrence + norm per
+    layer.  Every layer's output and state are checked on a rotating set of 4 heads; the
+    norm output of every layer on the same heads."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    for layer in range(36):
+        x = make_inputs(2048, seed=layer, with_norm=True)
+        d = to_dev(x)
+        heads = [(layer * 7 + j * 13) % 48 for j in range(4)]
+        o, s, o_ref, _ = _check("chunked", x, d, heads=heads, tag="layer%d" % layer)
+        y = gdn.out_norm(o, d["z"], d["w"], eps=1e-6)
+        torch.cuda.synchronize()
+        y_h = y.cpu().numpy()[:, heads]
+        y_ref = oracle.out_norm(o_ref, x["z"][:, heads], x["w"], 1e-6, heads=heads)
+        assert f16_ulp_distance(y_h, y_ref).max() <= 1
