@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=32768)
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the CPU-oracle sample (0 disables the CPU baseline)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -9,30 +9,33 @@ namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// DPP move within a row of 16 lanes (gfx9 DPP16 control codes).
+// DPP move within a row of 16 lanes (gfx9 DPP16 control codes).  Written as update_dpp
+// with old = 0 and bound_ctrl so that the compiler fuses the move into the consuming add
+// (one v_add_f32_dpp per step).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-constexpr int DPP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int DPP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within each 8 lanes
 constexpr int DPP_MIRROR = 0x140;       // lane i <- lane 15-i within each 16 lanes
+constexpr int SWIZZLE_XOR16 = 0x401F;   // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10
 
 // Sum over the 32 lanes of each half of the wave; every lane receives its half's sum.
-// Four DPP steps reduce inside a row of 16 lanes, then v_permlane16_swap exchanges the
-// two rows of each half (rows 0<->1 and 2<->3), so both rows hold the 32-lane total.
+// Four DPP steps reduce inside a row of 16 lanes; ds_swizzle (lane ^ 16 within each 32)
+// then adds the other row of the half.  (v_permlane16_swap would do this last step on the
+// VALU, but this compiler returns the same register for both results of its builtin.)
 // Must be executed by all 32 lanes of the half.
 __device__ __forceinline__ float half_wave_sum(float x) {
   x += dpp_mov<DPP_XOR1>(x);
   x += dpp_mov<DPP_XOR2>(x);
   x += dpp_mov<DPP_HALF_MIRROR>(x);
   x += dpp_mov<DPP_MIRROR>(x);
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                                                   SWIZZLE_XOR16));
 }
 
 // D = A * B + C on a 16x16 tile with a K-step of 4 (v_mfma_f32_16x16x4_f32).

@@ -1,8 +1,12 @@
 """Parity of the HIP path (through the C ABI) with the FP64 oracle, on the GPU.
 
 Gates (max|diff| / max|value| per tensor and call, against the oracle): 2e-6 for the
-sequential kernel, 5e-6 for the chunked kernels, for the outputs and the final state; the
-FP16 norm output within 1 unit in the last place.  Inputs are the seeded synthetic
+sequential kernel, 5e-6 for the chunked kernels, for the outputs and the final state.  The
+FP16 norm output is within 1 unit in the last place of the oracle's norm of the GPU's own
+FP32 output (the norm kernel alone), and within 1 ulp plus the recurrence gate's error
+carried through the norm, plus the reference's own rounding, of the oracle's norm of the
+oracle's output (end to end: a tiny o_j has a large relative error under a max-normalised
+gate, so a fixed number of ulps cannot hold there).  Inputs are the seeded synthetic
 workloads of the pages' parity test: T = 64, the edge-length sweep from a non-zero state,
 T = 8192 with the output norm, T = 32768 chunked, and a 36-layer stack at T = 2048.
 """
@@ -10,7 +14,8 @@ import numpy as np
 import pytest
 
 from conftest import rel_err
-from gpu_util import CHUNKED_TOL, SEQ_TOL, f16_ulp_distance, log, run, to_dev
+from gpu_util import (CHUNKED_TOL, SEQ_TOL, f16_ulp_distance, log, run, to_dev,
+                      y_end_to_end_violations)
 from linear_attention_recurrence_gated_amd.inputs import EDGE_LENGTHS, make_inputs
 
 torch = pytest.importorskip("torch")
@@ -161,11 +166,15 @@ def test_t8192_seq_and_norm():
     dist = f16_ulp_distance(y_h, y_iso)
     log("  norm isolated: max ulp %d, exact %.4f" % (dist.max(), (dist == 0).mean()))
     assert dist.max() <= 1
-    # end to end: the oracle norm of the oracle's FP64 recurrence output
+    # end to end: the oracle norm of the oracle's FP64 recurrence output, within one ulp
+    # plus the recurrence gate's error carried through the norm
     y_e2e = oracle.out_norm(o_ref, x["z"], x["w"], 1e-6)
     dist = f16_ulp_distance(y_h, y_e2e)
-    log("  norm end-to-end: max ulp %d, exact %.4f" % (dist.max(), (dist == 0).mean()))
-    assert dist.max() <= 1
+    bad, worst = y_end_to_end_violations(y_h, o_ref, x["z"], x["w"][None], 1e-6, SEQ_TOL,
+                                         y_e2e)
+    log("  norm end-to-end: max ulp %d, exact %.4f, outside bound %d %s"
+        % (dist.max(), (dist == 0).mean(), bad, worst))
+    assert bad == 0, worst
 
 
 def test_t32768_chunked_and_seq():
@@ -194,5 +203,12 @@ def test_36_layer_stack():
         y = gdn.out_norm(o, d["z"], d["w"], eps=1e-6)
         torch.cuda.synchronize()
         y_h = y.cpu().numpy()[:, heads]
+        # isolated (oracle norm of the GPU's own FP32 output): within one ulp
+        y_iso = oracle.out_norm(o.cpu().numpy()[:, heads], x["z"][:, heads], x["w"], 1e-6,
+                                heads=heads)
+        assert f16_ulp_distance(y_h, y_iso).max() <= 1
+        # end to end (oracle norm of the oracle's output): the propagated bound
         y_ref = oracle.out_norm(o_ref, x["z"][:, heads], x["w"], 1e-6, heads=heads)
-        assert f16_ulp_distance(y_h, y_ref).max() <= 1
+        bad, worst = y_end_to_end_violations(y_h, o_ref, x["z"][:, heads], x["w"][heads][None],
+                                             1e-6, CHUNKED_TOL, y_ref)
+        assert bad == 0, worst
