@@ -48,7 +48,7 @@ struct PrepSmem {
   float A[4][kChunk][kChunk];
 };
 
-__global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(ChunkArgs a) {
   __shared__ PrepSmem sm;
   const int c = blockIdx.x, kh = blockIdx.y;
   const int Hk = a.n_k_heads, Hv = a.n_v_heads, G = Hv / Hk;
@@ -111,8 +111,14 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(ChunkArgs a) {
     double gam_l = 0.0;
     if (active) {
       const int t = l & 31;
-      for (int s = 0; s < kChunk; ++s)
-        if (s <= t) gam_l += (double)sm.gs[m][s];  // inclusive running sum, in FP64
+#pragma unroll
+      for (int s4 = 0; s4 < kChunk / 4; ++s4) {  // inclusive running sum, in FP64
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.gs[m][4 * s4]);
+        gam_l += 4 * s4 + 0 <= t ? (double)g4.x : 0.0;
+        gam_l += 4 * s4 + 1 <= t ? (double)g4.y : 0.0;
+        gam_l += 4 * s4 + 2 <= t ? (double)g4.z : 0.0;
+        gam_l += 4 * s4 + 3 <= t ? (double)g4.w : 0.0;
+      }
       if (l < kChunk) sm.gam[w][t] = gam_l;
     }
     __syncthreads();
@@ -137,15 +143,29 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(ChunkArgs a) {
     __syncthreads();
     if (active && l < kChunk) {
       // Column j = l of T = (I + A)^-1 by forward substitution: row t of (I + A) T = I
-      // gives T[t][j] = [t == j] - sum_{i < t} A[t][i] T[i][j].
+      // gives T[t][j] = [t == j] - sum_{i < t} A[t][i] T[i][j].  Each row's sum runs in
+      // four independent partial sums (i mod 4), and row t+1 of A is read from LDS (as
+      // 16-byte broadcasts) before row t is computed, so neither the FMA chain nor the
+      // LDS latency serialises the solve.
       const int j = l;
       float Tc[kChunk];
+      f32x4 arow[2][kChunk / 4];
+#pragma unroll
+      for (int q4 = 0; q4 < kChunk / 4; ++q4)
+        arow[0][q4] = *reinterpret_cast<const f32x4*>(&sm.A[w][0][4 * q4]);
 #pragma unroll
       for (int t = 0; t < kChunk; ++t) {
-        float x = t == j ? 1.f : 0.f;
+        const int cb = t & 1;
+        if (t + 1 < kChunk) {
 #pragma unroll
-        for (int i = 0; i < t; ++i) x = fmaf(-sm.A[w][t][i], Tc[i], x);
-        Tc[t] = x;
+          for (int q4 = 0; q4 < kChunk / 4; ++q4)
+            if (4 * q4 < t + 1)
+              arow[cb ^ 1][q4] = *reinterpret_cast<const f32x4*>(&sm.A[w][t + 1][4 * q4]);
+        }
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < t; ++i) part[i & 3] = fmaf(arow[cb][i >> 2][i & 3], Tc[i], part[i & 3]);
+        Tc[t] = (t == j ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
       }
       const float bj = sm.bs[m][j];
 #pragma unroll
@@ -158,28 +178,37 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------------------
-template <int CSB>
+// One workgroup = one value head x 32 value columns: 4 waves, wave (cs, rh) owning value
+// columns 16 cs .. 16 cs + 15 of the workgroup and key rows 64 rh .. 64 rh + 63.  Every
+// operand a chunk needs (K and Q rows of the key head, the head's WY slot from the
+// workspace and the workgroup's V tile) is staged into LDS once per workgroup with
+// coalesced 16-byte loads, one chunk ahead, and read from LDS by the waves; only the
+// outputs go straight to memory.
+constexpr int SC_NT = 256;  // threads per scan workgroup
+constexpr int SC_COLS = 32; // value columns per scan workgroup
+constexpr int TPAD = 36;    // LDS row stride of T, P and V^T (floats): conflict-free reads
+
 struct ScanSmem {
   float k[2][kChunk][KP];
   float q[2][kChunk][KP];
-  f32x4 x[2][CSB][2][3][64];  // partial-sum exchange: [parity][col slice][row half][tile][lane]
+  float T[2][kChunk][TPAD];        // T diag(beta)
+  float P[2][kChunk][TPAD];
+  float vt[2][SC_COLS][TPAD];      // V^T: [column of the workgroup][token]
+  float eg[2][kChunk], eb[2][kChunk], egl[2][4];
+  f32x4 x[2][2][2][4][64];         // exchange: [parity][col slice][row half][tile][lane]
 };
 
-// Per-wave operands of one chunk, prefetched from global memory one chunk ahead.
-struct ScanOps {
-  float v[2][4];  // V[16tt + 4(l/16) + r][col]
-  f32x4 T00, T10, T11;  // T diag(beta) blocks, MFMA A-operand order
-  f32x4 Pa, Pb;         // P blocks (rh,0) and (1,1) (Pb used by rh = 1 only)
-  f32x4 eg[2], eb[2];
-  float egl;
+// Global loads of one chunk's operands, held in registers until written to LDS.
+struct ScanStage {
+  f32x4 k[4], q[4];  // K/Q rows: float4 index tid + 256 i of the 32 x 32 float4 tile
+  f32x4 slot[3];     // workspace slot: float4 index tid + 256 i (< 544)
+  f32x4 v;           // V: token tid / 8, columns 4 (tid % 8) .. +3
 };
 
-template <int CSB>
-__global__ __launch_bounds__(128 * CSB) void chunk_scan_kernel(ChunkArgs a) {
-  constexpr int NT = 128 * CSB;
-  constexpr int NCB = kDim / (16 * CSB);       // column blocks per value head
-  constexpr int KQ_F4 = 2 * kChunk * 32 / NT;  // float4 of K and Q staged per thread
-  __shared__ ScanSmem<CSB> sm;
+__global__ __launch_bounds__(SC_NT) void chunk_scan_kernel(ChunkArgs a) {
+  constexpr int NCB = kDim / SC_COLS;  // column blocks per value head
+  constexpr int SLOT_F4 = kSlot / 4;   // 544
+  __shared__ ScanSmem sm;
 
   const int Hk = a.n_k_heads, Hv = a.n_v_heads, G = Hv / Hk;
   const int L = xcd_grouped_block(blockIdx.x, gridDim.x);
@@ -188,7 +217,8 @@ __global__ __launch_bounds__(128 * CSB) void chunk_scan_kernel(ChunkArgs a) {
   const int h = kh + m * Hk;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int cs = w >> 1, rh = w & 1;
-  const int col = cblk * 16 * CSB + 16 * cs + (l & 15);
+  const int colw = 16 * cs + (l & 15);      // column inside the workgroup
+  const int col = cblk * SC_COLS + colw;    // value column
   const int lr = 4 * (l >> 4);  // row offset of this lane inside a 16-row MFMA tile
   const int nch = (a.n_tok + kChunk - 1) / kChunk;
 
@@ -200,86 +230,64 @@ __global__ __launch_bounds__(128 * CSB) void chunk_scan_kernel(ChunkArgs a) {
     for (int r = 0; r < 4; ++r)
       S[rt][r] = a.s_src[((size_t)h * kDim + 64 * rh + 16 * rt + lr + r) * kDim + col];
 
-  auto load_ops = [&](ScanOps& op, int c) {
-    const float* slot = a.ws + ((size_t)c * Hv + h) * kSlot;
-    const int c0 = c * kChunk;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tk = c0 + 16 * tt + lr + r;
-        op.v[tt][r] =
-            tk < a.n_tok ? a.v[((size_t)(a.t_begin + tk) * Hv + h) * kDim + col] : 0.f;
-      }
-    const int arow = (l & 15) * kChunk + lr;
-    op.T00 = *reinterpret_cast<const f32x4*>(slot + kSlotT + arow);
-    op.T10 = *reinterpret_cast<const f32x4*>(slot + kSlotT + 16 * kChunk + arow);
-    op.T11 = *reinterpret_cast<const f32x4*>(slot + kSlotT + 16 * kChunk + 16 + arow);
-    op.Pa = *reinterpret_cast<const f32x4*>(slot + kSlotP + 16 * rh * kChunk + arow);
-    op.Pb = *reinterpret_cast<const f32x4*>(slot + kSlotP + 16 * kChunk + 16 + arow);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      op.eg[tt] = *reinterpret_cast<const f32x4*>(slot + kSlotEg + 16 * tt + lr);
-      op.eb[tt] = *reinterpret_cast<const f32x4*>(slot + kSlotEb + 16 * tt + lr);
-    }
-    op.egl = slot[kSlotEgl];
-  };
+  // The super-block's tokens, addressed through bounds-checked buffer resources: reads
+  // past its last token return 0 (the zero padding of a partial chunk), writes past it are
+  // dropped.  Byte offsets stay far below 2^32 (at most 2048 tokens per super-block).
+  const buf_rsrc rs_k = make_rsrc(a.k + (size_t)a.t_begin * Hk * kDim, a.n_tok * Hk * kDim * 4);
+  const buf_rsrc rs_q = make_rsrc(a.q + (size_t)a.t_begin * Hk * kDim, a.n_tok * Hk * kDim * 4);
+  const buf_rsrc rs_v = make_rsrc(a.v + (size_t)a.t_begin * Hv * kDim, a.n_tok * Hv * kDim * 4);
+  const buf_rsrc rs_o = make_rsrc(a.o + (size_t)a.t_begin * Hv * kDim, a.n_tok * Hv * kDim * 4);
 
-  float4 kst[KQ_F4 / 2], qst[KQ_F4 / 2];
+  ScanStage st;
+  // Global loads for chunk c (the workspace slot is clamped to the last chunk, so loads
+  // past the end stay inside the workspace; tokens past the end read as 0).  Every thread
+  // issues the same loads in every chunk, so the compiler's wait counts stay exact.
   auto stage_load = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < KQ_F4 / 2; ++i) {
-      const int f = tid + NT * i, tt = f >> 5, p = f & 31;
-      const int tk = c * kChunk + tt;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-      if (tk < a.n_tok) {
-        const size_t off = ((size_t)(a.t_begin + tk) * Hk + kh) * kDim + 4 * p;
-        kv = *reinterpret_cast<const float4*>(a.k + off);
-        qv = *reinterpret_cast<const float4*>(a.q + off);
-      }
-      kst[i] = kv;
-      qst[i] = qv;
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + SC_NT * i, tt = f >> 5, p = f & 31;
+      const int off = (((c * kChunk + tt) * Hk + kh) * kDim + 4 * p) * 4;
+      st.k[i] = buf_load4(rs_k, off);
+      st.q[i] = buf_load4(rs_q, off);
     }
-  };
-  auto stage_store = [&](int buf) {
+    const f32x4* slot =
+        reinterpret_cast<const f32x4*>(a.ws + ((size_t)min(c, nch - 1) * Hv + h) * kSlot);
 #pragma unroll
-    for (int i = 0; i < KQ_F4 / 2; ++i) {
-      const int f = tid + NT * i, tt = f >> 5, p = f & 31;
-      *reinterpret_cast<float4*>(&sm.k[buf][tt][4 * p]) = kst[i];
-      *reinterpret_cast<float4*>(&sm.q[buf][tt][4 * p]) = qst[i];
+    for (int i = 0; i < 3; ++i) st.slot[i] = slot[min(tid + SC_NT * i, SLOT_F4 - 1)];
+    st.v = buf_load4(rs_v, (((c * kChunk + (tid >> 3)) * Hv + h) * kDim + cblk * SC_COLS +
+                            4 * (tid & 7)) * 4);
+  };
+  auto stage_store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + SC_NT * i, tt = f >> 5, p = f & 31;
+      *reinterpret_cast<f32x4*>(&sm.k[b][tt][4 * p]) = st.k[i];
+      *reinterpret_cast<f32x4*>(&sm.q[b][tt][4 * p]) = st.q[i];
     }
+    // slot float4 f: T rows (f < 256), P rows (f < 512), then e^gamma, e^(last-gamma), e^last
+    *reinterpret_cast<f32x4*>(&sm.T[b][tid >> 3][4 * (tid & 7)]) = st.slot[0];
+    *reinterpret_cast<f32x4*>(&sm.P[b][tid >> 3][4 * (tid & 7)]) = st.slot[1];
+    if (tid < 8) *reinterpret_cast<f32x4*>(&sm.eg[b][4 * tid]) = st.slot[2];
+    else if (tid < 16) *reinterpret_cast<f32x4*>(&sm.eb[b][4 * (tid - 8)]) = st.slot[2];
+    else if (tid == 16) *reinterpret_cast<f32x4*>(&sm.egl[b][0]) = st.slot[2];
+    const int vt_tok = tid >> 3, vt_col = 4 * (tid & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.vt[b][vt_col + i][vt_tok] = st.v[i];
   };
 
-  ScanOps cur, nxt;
-  stage_load(0);
-  stage_store(0);
-  if (nch > 1) stage_load(1);
-  load_ops(cur, 0);
-  __syncthreads();
-
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1, par = c & 1;
-    // (a) partial K S0 and Q S0 over this wave's 64 rows; K^T operands for the update.
-    f32x4 W[2], QS[2];
+  auto chunk_step = [&](int c) {
+    const int buf = c & 1;
+    // (a) operands of this chunk from LDS (written before the previous chunk's barrier),
+    //     then partial K S0 and Q S0 over this wave's 64 rows.
+    f32x4 ka[4][2], qa[4][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      W[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      QS[tt] = W[tt];
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int row = 64 * rh + 16 * rt + lr;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 ka = *reinterpret_cast<const f32x4*>(&sm.k[buf][16 * tt + (l & 15)][row]);
-        const f32x4 qa = *reinterpret_cast<const f32x4*>(&sm.q[buf][16 * tt + (l & 15)][row]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          W[tt] = mfma16x16x4(ka[r], S[rt][r], W[tt]);
-          QS[tt] = mfma16x16x4(qa[r], S[rt][r], QS[tt]);
-        }
+        const int row = 64 * rh + 16 * rt + lr;
+        ka[rt][tt] = *reinterpret_cast<const f32x4*>(&sm.k[buf][16 * tt + (l & 15)][row]);
+        qa[rt][tt] = *reinterpret_cast<const f32x4*>(&sm.q[buf][16 * tt + (l & 15)][row]);
       }
-    }
     float kt[4][2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -288,69 +296,102 @@ __global__ __launch_bounds__(128 * CSB) void chunk_scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           kt[rt][tt][r] = sm.k[buf][16 * tt + lr + r][64 * rh + 16 * rt + (l & 15)];
-
-    // (a') stage the next chunk's K/Q into the other LDS buffer (last read in chunk c-1,
-    //      before that chunk's barrier), then start loading the one after it.
-    if (c + 1 < nch) {
-      stage_store(buf ^ 1);
-      if (c + 2 < nch) stage_load(c + 2);
-      load_ops(nxt, c + 1);
+    const int ar = l & 15;
+    const f32x4 T00 = *reinterpret_cast<const f32x4*>(&sm.T[buf][ar][lr]);
+    const f32x4 T10 = *reinterpret_cast<const f32x4*>(&sm.T[buf][16 + ar][lr]);
+    const f32x4 T11 = *reinterpret_cast<const f32x4*>(&sm.T[buf][16 + ar][16 + lr]);
+    const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sm.P[buf][16 * rh + ar][lr]);
+    const f32x4 Pb = *reinterpret_cast<const f32x4*>(&sm.P[buf][16 + ar][16 + lr]);
+    f32x4 eg[2], eb[2], vv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      eg[tt] = *reinterpret_cast<const f32x4*>(&sm.eg[buf][16 * tt + lr]);
+      eb[tt] = *reinterpret_cast<const f32x4*>(&sm.eb[buf][16 * tt + lr]);
+      vv[tt] = *reinterpret_cast<const f32x4*>(&sm.vt[buf][colw][16 * tt + lr]);
     }
+    const float egl = sm.egl[buf][0];
 
-    // (b) exchange partial sums with the other row half of the same columns.
-    sm.x[par][cs][rh][0][l] = W[0];
-    sm.x[par][cs][rh][1][l] = W[1];
-    // (selects, not QS[rh]: a runtime index would push the array out of registers)
-    sm.x[par][cs][rh][2][l] = rh ? QS[0] : QS[1];
+    f32x4 P4[4];  // partial W0, W1, QS0, QS1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) P4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          P4[tt] = mfma16x16x4(ka[rt][tt][r], S[rt][r], P4[tt]);
+          P4[2 + tt] = mfma16x16x4(qa[rt][tt][r], S[rt][r], P4[2 + tt]);
+        }
+
+    // (a') stage chunk c+1 into the other LDS buffer (its last reads were in chunk c-1's
+    //      phase (a), before that chunk's barrier), then load chunk c+2.
+    stage_store(buf ^ 1);
+    stage_load(c + 2);
+
+    // (b) exchange partial sums with the other row half of the same columns; both halves
+    //     add the two halves in the same order, so they hold identical sums.
+    const int par = c & 1;
+    sm.x[par][cs][rh][0][l] = P4[0];
+    sm.x[par][cs][rh][1][l] = P4[1];
+    sm.x[par][cs][rh][2][l] = rh ? P4[2] : P4[3];  // the other half's output tile
     __syncthreads();
-    W[0] += sm.x[par][cs][1 - rh][0][l];
-    W[1] += sm.x[par][cs][1 - rh][1][l];
-    const f32x4 QSf = (rh ? QS[1] : QS[0]) + sm.x[par][cs][1 - rh][2][l];
+    f32x4 W[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) W[tt] = sm.x[par][cs][0][tt][l] + sm.x[par][cs][1][tt][l];
+    const f32x4 QSo = sm.x[par][cs][1 - rh][2][l];
+    const f32x4 QSf = rh ? (QSo + P4[3]) : (P4[2] + QSo);
 
     // (c) U = V - e^{gamma} (K S0), C layout: token 16 tt + lr + r, column col.
     f32x4 U[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) U[tt][r] = fmaf(-cur.eg[tt][r], W[tt][r], cur.v[tt][r]);
+      for (int r = 0; r < 4; ++r) U[tt][r] = fmaf(-eg[tt][r], W[tt][r], vv[tt][r]);
 
     // (d) D = T diag(beta) U; T is lower triangular, so tile (0,1) is zero.
     f32x4 D[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) D[0] = mfma16x16x4(cur.T00[r], U[0][r], D[0]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) D[1] = mfma16x16x4(cur.T10[r], U[0][r], D[1]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) D[1] = mfma16x16x4(cur.T11[r], U[1][r], D[1]);
-
-    // (e) outputs of token tile rh: O = e^{gamma} Q S0 + P D (P lower triangular).
-    f32x4 O = (rh ? cur.eg[1] : cur.eg[0]) * QSf;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) O = mfma16x16x4(cur.Pa[r], D[0][r], O);
-    if (rh == 1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O = mfma16x16x4(cur.Pb[r], D[1][r], O);
+    for (int r = 0; r < 4; ++r) {
+      D[0] = mfma16x16x4(T00[r], U[0][r], D[0]);
+      D[1] = mfma16x16x4(T10[r], U[0][r], D[1]);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; ++r) D[1] = mfma16x16x4(T11[r], U[1][r], D[1]);
+
+    // (e) outputs of token tile rh: O = e^{gamma} Q S0 + P D (P lower triangular).
+    f32x4 O = (rh ? eg[1] : eg[0]) * QSf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) O = mfma16x16x4(Pa[r], D[0][r], O);
+    if (rh == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O = mfma16x16x4(Pb[r], D[1][r], O);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // dropped by the buffer past the last token
       const int tk = c * kChunk + 16 * rh + lr + r;
-      if (tk < a.n_tok) a.o[((size_t)(a.t_begin + tk) * Hv + h) * kDim + col] = O[r];
+      buf_store(rs_o, ((tk * Hv + h) * kDim + col) * 4, O[r]);
     }
 
     // (f, g) S' = e^{gamma_last} S0 + K^T diag(e^{gamma_last - gamma}) D.
     f32x4 Dh[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) Dh[tt] = cur.eb[tt] * D[tt];
+    for (int tt = 0; tt < 2; ++tt) Dh[tt] = eb[tt] * D[tt];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      S[rt] = cur.egl * S[rt];
+    for (int rt = 0; rt < 4; ++rt) S[rt] = egl * S[rt];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[rt] = mfma16x16x4(kt[rt][tt][r], Dh[tt][r], S[rt]);
-    }
-    cur = nxt;
-  }
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) S[rt] = mfma16x16x4(kt[rt][tt][r], Dh[tt][r], S[rt]);
+  };
+
+  stage_load(0);
+  stage_store(0);
+  stage_load(1);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) chunk_step(c);
 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -358,8 +399,6 @@ __global__ __launch_bounds__(128 * CSB) void chunk_scan_kernel(ChunkArgs a) {
     for (int r = 0; r < 4; ++r)
       a.s_dst[((size_t)h * kDim + 64 * rh + 16 * rt + lr + r) * kDim + col] = S[rt][r];
 }
-
-constexpr int kScanCSB = 2;
 
 }  // namespace
 
@@ -372,9 +411,9 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream) {
 
 hipError_t launch_chunk_scan(const ChunkArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<ChunkArgs*>(&a)};
-  const int nblocks = a.n_v_heads * (kDim / (16 * kScanCSB));
-  return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_scan_kernel<kScanCSB>),
-                         dim3(nblocks), dim3(128 * kScanCSB), args, 0, stream);
+  const int nblocks = a.n_v_heads * (kDim / SC_COLS);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_scan_kernel), dim3(nblocks),
+                         dim3(SC_NT), args, 0, stream);
 }
 
 }  // namespace gdn

@@ -45,6 +45,28 @@ __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Raw buffer resources: the hardware checks every access against num_records, so a load
+// past the end returns 0 and a store past the end is dropped.  Ragged tails therefore need
+// no branches, every lane issues the same memory operations, and per-lane offsets are
+// 32-bit byte offsets from a base held in scalar registers.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kBufferDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufferDword3);
+}
+// (the b32 builtins move raw 32-bit words: reinterpret the bits, never convert the value)
+__device__ __forceinline__ float buf_load(buf_rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ f32x4 buf_load4(buf_rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ void buf_store(buf_rsrc r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).  This
 // maps a workgroup id to a logical block so that consecutive logical blocks share an XCD
 // (and its L2): XCD x receives the logical range [x*n/8, (x+1)*n/8).

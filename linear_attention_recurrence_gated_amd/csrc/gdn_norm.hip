@@ -8,8 +8,9 @@
 //
 // Bound by HBM traffic (read o and z, write y: 1280 bytes per row): each half-wave owns a
 // row (16 bytes of o and of z per lane, one coalesced 512-byte load each), the sum of
-// squares is reduced inside the half-wave with DPP, and a grid-stride loop keeps two rows
-// per half-wave in flight.
+// squares is reduced inside the half-wave with DPP, and a grid-stride loop issues the
+// loads of four rows per half-wave before any arithmetic, with non-temporal (streaming)
+// loads and stores since every byte is touched once.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -26,37 +27,44 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-__device__ __forceinline__ void norm_row(const NormArgs& a, int row, int p,
-                                         const float4 ov, const float4 zv) {
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void norm_row(const NormArgs& a, int row, int p, const f32x4 ov,
+                                         const f32x4 zv) {
   const int h = row % a.n_v_heads;
   const float4 wv = *reinterpret_cast<const float4*>(a.w + h * kDim + 4 * p);
   float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
   ss = half_wave_sum(ss);
   const float rs = 1.0f / sqrtf(ss * (1.0f / kDim) + a.eps);
-  uint2 out;
+  u32x2 out;
   out.x = pack_half2(ov.x * rs * wv.x * sigmoid(zv.x), ov.y * rs * wv.y * sigmoid(zv.y));
   out.y = pack_half2(ov.z * rs * wv.z * sigmoid(zv.z), ov.w * rs * wv.w * sigmoid(zv.w));
-  *reinterpret_cast<uint2*>(a.y + row * kDim + 4 * p) = out;
+  __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(a.y + row * kDim + 4 * p));
 }
+
+constexpr int ROWS = 4;  // rows per half-wave per iteration, all loaded before any math
 
 __global__ __launch_bounds__(NT) void out_norm_kernel(NormArgs a) {
   const int p = threadIdx.x & 31;
-  const int rows_per_iter = gridDim.x * (NT / 32);
-  int row = blockIdx.x * (NT / 32) + (threadIdx.x >> 5);
-  // two rows per half-wave per iteration; each half-wave's row is uniform across it
-  for (; row + rows_per_iter < a.n_rows; row += 2 * rows_per_iter) {
-    const int row2 = row + rows_per_iter;
-    const float4 o1 = *reinterpret_cast<const float4*>(a.o + row * kDim + 4 * p);
-    const float4 z1 = *reinterpret_cast<const float4*>(a.z + row * kDim + 4 * p);
-    const float4 o2 = *reinterpret_cast<const float4*>(a.o + row2 * kDim + 4 * p);
-    const float4 z2 = *reinterpret_cast<const float4*>(a.z + row2 * kDim + 4 * p);
-    norm_row(a, row, p, o1, z1);
-    norm_row(a, row2, p, o2, z2);
-  }
-  if (row < a.n_rows) {
-    const float4 o1 = *reinterpret_cast<const float4*>(a.o + row * kDim + 4 * p);
-    const float4 z1 = *reinterpret_cast<const float4*>(a.z + row * kDim + 4 * p);
-    norm_row(a, row, p, o1, z1);
+  const int hw = blockIdx.x * (NT / 32) + (threadIdx.x >> 5);  // this half-wave
+  const int nhw = gridDim.x * (NT / 32);
+  // Rows hw, hw + nhw, hw + 2 nhw, ...; each half-wave's row is uniform across its 32
+  // lanes, so the conditions below never split a half-wave.
+  for (int row = hw; row < a.n_rows; row += ROWS * nhw) {
+    f32x4 ov[ROWS], zv[ROWS];
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u) {
+      const int r = row + u * nhw;
+      if (r < a.n_rows) {
+        ov[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.o + r * kDim) + p);
+        zv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.z + r * kDim) + p);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u) {
+      const int r = row + u * nhw;
+      if (r < a.n_rows) norm_row(a, r, p, ov[u], zv[u]);
+    }
   }
 }
 
@@ -64,9 +72,9 @@ __global__ __launch_bounds__(NT) void out_norm_kernel(NormArgs a) {
 
 hipError_t launch_out_norm(const NormArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<NormArgs*>(&a)};
-  const int rows_per_block = NT / 32;
+  const int rows_per_block = (NT / 32) * ROWS;
   int nblocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
-  const int cap = 256 * 16;  // 16 workgroups per CU, then grid-stride
+  const int cap = 256 * 8;  // 8 workgroups per CU (32 waves), then grid-stride
   if (nblocks > cap) nblocks = cap;
   return hipLaunchKernel(reinterpret_cast<const void*>(&out_norm_kernel), dim3(nblocks),
                          dim3(NT), args, 0, stream);
