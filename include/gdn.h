@@ -76,10 +76,10 @@ int gdn_recurrence_seq(const float* q, const float* k, const float* v, const flo
 
 /*
  * Bytes of caller-owned device scratch that gdn_recurrence_chunked needs.  It does not
- * depend on T: the scratch holds the per-chunk operators of one 2048-token super-block
- * ("#1372 DeltaNet recurrence: STRATA_GDN_CHUNKED=1", section "What it does", paragraph
- * "Scratch": the prep output of one super-block, allocated once per device and kept).
- * Returns 0 for an unsupported shape.
+ * depend on T: the scratch holds the per-chunk operators of two 2048-token super-blocks,
+ * the one being scanned and the next one being prepared ("#1372 DeltaNet recurrence:
+ * STRATA_GDN_CHUNKED=1", section "What it does", paragraph "Scratch": the prep output of
+ * a super-block, allocated once per device and kept).  Returns 0 for an unsupported shape.
  */
 size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv);
 
@@ -94,7 +94,9 @@ size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv)
  *     S' = e^{gamma_last} S0 + K^T e^{gamma_last - gamma} D.
  * A prep kernel forms the chunk operators for every chunk of a 2048-token super-block at
  * once; a scan kernel then walks the super-block's chunks carrying the state on chip.
- * The state passes between super-blocks through state_out.  A last partial chunk is
+ * The scan launch of super-block n also carries the prep of super-block n+1 on the
+ * compute units the scan leaves idle.  The state passes between super-blocks through
+ * state_out.  A last partial chunk is
  * padded with zero tokens (g = 0, beta = 0), which leave the state unchanged.
  *
  *   workspace, workspace_bytes : device scratch of at least

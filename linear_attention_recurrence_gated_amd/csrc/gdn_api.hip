@@ -107,7 +107,8 @@ int gdn_recurrence_seq(const float* q, const float* k, const float* v, const flo
 
 size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv) {
   if (check_shape(0, n_k_heads, n_v_heads, dk, dv) != GDN_OK) return 0;
-  return (size_t)gdn::kChunksPerSB * n_v_heads * gdn::kSlot * sizeof(float);
+  // two halves: one super-block's operators are scanned while the next one's are formed
+  return 2 * (size_t)gdn::kChunksPerSB * n_v_heads * gdn::kSlot * sizeof(float);
 }
 
 }  // extern "C"
@@ -125,18 +126,28 @@ int chunked_impl(const float* q, const float* k, const float* v, const float* g,
   if (n_scan_events > 0 && !scan_events) return GDN_ERR_NULL_POINTER;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) return copy_state_if_needed(state_in, state_out, n_v_heads, dk, dv, s);
-  int sb = 0;
-  for (int64_t t0 = 0; t0 < T; t0 += gdn::kSuperBlock, ++sb) {
+  // Workspace halves alternate between super-blocks: launch sb scans super-block sb from
+  // half sb % 2 while its extra workgroups prepare super-block sb + 1 into the other half.
+  const size_t half_floats = (size_t)gdn::kChunksPerSB * n_v_heads * gdn::kSlot;
+  const int nsb = (int)((T + gdn::kSuperBlock - 1) / gdn::kSuperBlock);
+  auto sb_args = [&](int sb) {
+    const int64_t t0 = (int64_t)sb * gdn::kSuperBlock;
     const int n = (int)((T - t0) < gdn::kSuperBlock ? (T - t0) : gdn::kSuperBlock);
-    gdn::ChunkArgs a{q, k, v, g, beta, t0 == 0 ? state_in : state_out, state_out, o,
-                     static_cast<float*>(workspace), (int)t0, n, n_k_heads, n_v_heads};
-    hipError_t e = gdn::launch_chunk_prep(a, s);
-    if (e != hipSuccess) return hip_fail(e);
+    return gdn::ChunkArgs{q, k, v, g, beta, t0 == 0 ? state_in : state_out, state_out, o,
+                          static_cast<float*>(workspace) + (sb & 1) * half_floats, (int)t0, n,
+                          n_k_heads, n_v_heads};
+  };
+  const gdn::ChunkArgs first = sb_args(0);
+  hipError_t e = gdn::launch_chunk_prep(first, s);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int sb = 0; sb < nsb; ++sb) {
+    const gdn::ChunkArgs a = sb_args(sb);
+    const gdn::ChunkArgs next = sb + 1 < nsb ? sb_args(sb + 1) : a;
     const bool timed = 2 * sb + 1 < n_scan_events;
     if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(scan_events[2 * sb]), s)) !=
                      hipSuccess)
       return hip_fail(e);
-    e = gdn::launch_chunk_scan(a, s);
+    e = gdn::launch_chunk_scan_fused(a, sb + 1 < nsb ? &next : nullptr, s);
     if (e != hipSuccess) return hip_fail(e);
     if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(scan_events[2 * sb + 1]), s)) !=
                      hipSuccess)

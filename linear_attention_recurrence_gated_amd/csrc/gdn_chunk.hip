@@ -48,9 +48,10 @@ struct PrepSmem {
   float A[4][kChunk][kChunk];
 };
 
-__global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(ChunkArgs a) {
-  __shared__ PrepSmem sm;
-  const int c = blockIdx.x, kh = blockIdx.y;
+// The operators of chunk c for key head kh and its value heads.  Called by every thread
+// of a 256-thread workgroup (it contains barriers); ends with a barrier, so one
+// workgroup may process several items in a row.
+__device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, PrepSmem& sm) {
   const int Hk = a.n_k_heads, Hv = a.n_v_heads, G = Hv / Hk;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int c0 = c * kChunk;  // first token of the chunk, relative to the super-block
@@ -205,13 +206,13 @@ struct ScanStage {
   f32x4 v;           // V: token tid / 8, columns 4 (tid % 8) .. +3
 };
 
-__global__ __launch_bounds__(SC_NT) void chunk_scan_kernel(ChunkArgs a) {
+// One scan workgroup (block index `b` of `nb` scan workgroups).
+__device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, ScanSmem& sm) {
   constexpr int NCB = kDim / SC_COLS;  // column blocks per value head
   constexpr int SLOT_F4 = kSlot / 4;   // 544
-  __shared__ ScanSmem sm;
 
   const int Hk = a.n_k_heads, Hv = a.n_v_heads, G = Hv / Hk;
-  const int L = xcd_grouped_block(blockIdx.x, gridDim.x);
+  const int L = xcd_grouped_block(b, nb);
   // logical order: key head, then value head of the group, then column block
   const int kh = L / (G * NCB), m = (L / NCB) % G, cblk = L % NCB;
   const int h = kh + m * Hk;
@@ -400,6 +401,43 @@ __global__ __launch_bounds__(SC_NT) void chunk_scan_kernel(ChunkArgs a) {
       a.s_dst[((size_t)h * kDim + 64 * rh + 16 * rt + lr + r) * kDim + col] = S[rt][r];
 }
 
+// Prep alone: one workgroup per (chunk, key head) of a super-block.
+__global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(ChunkArgs a) {
+  __shared__ PrepSmem sm;
+  prep_item(a, blockIdx.x, blockIdx.y, sm);
+}
+
+// Scan of super-block n fused with the prep of super-block n+1: workgroups
+// [0, n_scan) scan (they are dispatched first and take one CU each), the rest loop over
+// the (chunk, key head) items of the next super-block on the CUs the scan leaves idle.
+// The two roles touch disjoint halves of the workspace, and the next launch reads what
+// this one's prep wrote, so the roles never wait for each other.
+struct FusedArgs {
+  ChunkArgs scan;
+  ChunkArgs prep;
+  int n_scan;  // scan workgroups
+  int has_prep;
+};
+
+union FusedSmem {
+  ScanSmem scan;
+  PrepSmem prep;
+};
+
+__global__ __launch_bounds__(SC_NT) void chunk_fused_kernel(FusedArgs f) {
+  static_assert(SC_NT == PREP_NT, "both roles run with the same workgroup size");
+  __shared__ FusedSmem sm;
+  const int b = blockIdx.x;
+  if (b < f.n_scan) {
+    scan_block(f.scan, b, f.n_scan, sm.scan);
+  } else if (f.has_prep) {
+    const int Hk = f.prep.n_k_heads;
+    const int items = ((f.prep.n_tok + kChunk - 1) / kChunk) * Hk;
+    const int n_prep = gridDim.x - f.n_scan;
+    for (int it = b - f.n_scan; it < items; it += n_prep) prep_item(f.prep, it / Hk, it % Hk, sm.prep);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream) {
@@ -409,11 +447,22 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream) {
                          dim3(nch, a.n_k_heads), dim3(PREP_NT), args, 0, stream);
 }
 
-hipError_t launch_chunk_scan(const ChunkArgs& a, hipStream_t stream) {
-  void* args[] = {const_cast<ChunkArgs*>(&a)};
-  const int nblocks = a.n_v_heads * (kDim / SC_COLS);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_scan_kernel), dim3(nblocks),
-                         dim3(SC_NT), args, 0, stream);
+hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_next,
+                                   hipStream_t stream) {
+  FusedArgs f;
+  f.scan = scan;
+  f.prep = prep_next ? *prep_next : scan;
+  f.n_scan = scan.n_v_heads * (kDim / SC_COLS);
+  f.has_prep = prep_next != nullptr;
+  // the prep workgroups fill the CUs the scan leaves free (at least 32 of them)
+  int n_prep = 0;
+  if (prep_next) {
+    n_prep = kNumCUs - f.n_scan;
+    if (n_prep < 32) n_prep = 32;
+  }
+  void* args[] = {&f};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_fused_kernel),
+                         dim3(f.n_scan + n_prep), dim3(SC_NT), args, 0, stream);
 }
 
 }  // namespace gdn

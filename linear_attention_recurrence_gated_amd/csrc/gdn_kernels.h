@@ -9,6 +9,7 @@
 namespace gdn {
 
 constexpr int kDim = 128;          // dk = dv supported by every kernel
+constexpr int kNumCUs = 256;       // compute units of an MI355X
 constexpr int kMaxGroup = 4;       // value heads per key head supported
 constexpr int kChunk = 32;         // tokens per WY chunk
 constexpr int kSuperBlock = 2048;  // tokens whose chunk operators are prepared at once
@@ -64,7 +65,10 @@ struct NormArgs {
 
 hipError_t launch_seq(const SeqArgs& a, int group, hipStream_t stream);
 hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
-hipError_t launch_chunk_scan(const ChunkArgs& a, hipStream_t stream);
+// Scan of super-block `scan`; if prep_next is not NULL the same launch also forms the
+// operators of the next super-block (into prep_next->ws, the other workspace half).
+hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_next,
+                                   hipStream_t stream);
 hipError_t launch_out_norm(const NormArgs& a, hipStream_t stream);
 
 }  // namespace gdn

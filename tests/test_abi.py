@@ -46,7 +46,7 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_size(L):
-    assert L.gdn_chunked_workspace_bytes(16, 48, 128, 128) == 64 * 48 * 2176 * 4
+    assert L.gdn_chunked_workspace_bytes(16, 48, 128, 128) == 2 * 64 * 48 * 2176 * 4
     assert L.gdn_chunked_workspace_bytes(16, 48, 64, 128) == 0
     assert L.gdn_chunked_workspace_bytes(16, 40, 128, 128) == 0
     assert L.gdn_chunked_workspace_bytes(1, 5, 128, 128) == 0   # at most 4 value heads per key head
@@ -65,7 +65,7 @@ def _addrs(T=64, Hk=16, Hv=48):
     a = {}
     cur = BASE
     for name, size in (("q", qk), ("k", qk), ("v", vv), ("g", gb), ("beta", gb),
-                       ("s_in", st), ("s_out", st), ("o", vv), ("ws", 64 * Hv * 2176 * 4)):
+                       ("s_in", st), ("s_out", st), ("o", vv), ("ws", 2 * 64 * Hv * 2176 * 4)):
         a[name] = cur
         cur += (size + MB) & ~(MB - 1)
     return a
