@@ -68,19 +68,42 @@ class HipEvents:
             self.L.hipEventDestroy(ctypes.c_void_p(e))
 
 
+KERNEL_SOURCES = ("gdn_chunk.hip", "gdn_common.h", "gdn_kernels.h")
+
+
+def kernel_source_sha256():
+    """Hash of the sources the chunked kernels are built from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "linear_attention_recurrence_gated_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile():
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
-    taken on the current scan kernel source (else None)."""
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), if it was taken
+    on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "chunk_scan_traffic.json")
-    src = os.path.join(ROOT, "linear_attention_recurrence_gated_amd", "csrc", "gdn_chunk.hip")
     try:
-        rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_sha256") != kernel_source_sha256():
             return None
         return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
+
+
+def calibration_copy():
+    """A plain device copy of exactly 256 MiB (read 256 MiB, write 256 MiB), run twice, so
+    that rocprofv3's FETCH_SIZE / WRITE_SIZE can be scaled to bytes."""
+    import torch
+    a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(x, tokens):
@@ -107,6 +130,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the CPU-oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (for counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -177,6 +202,9 @@ def main():
     seq_ms = hip.elapsed_ms(evs[0], evs[1])
     hip.destroy(evs)
 
+    if args.calibration_copy:
+        calibration_copy()
+
     cpu = None
     if args.cpu_tokens > 0:
         print("bench: CPU oracle on %d tokens" % args.cpu_tokens, file=sys.stderr, flush=True)
@@ -205,7 +233,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "chunk_scan_kernel",
+            "kernel": "chunk_fused_kernel (scan of super-block n + prep of n+1)",
             "achieved": round(achieved, 3),
             "peak": PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s",

@@ -13,9 +13,9 @@
 //  - a 64-lane wave holds 2 value columns; the 32 lanes of a column each own 4 of the 128
 //    key rows of G state columns (4G floats of state per lane, in VGPRs for the whole
 //    sequence);
-//  - the kv and output sums over the 128 rows are reduced across the 32 lanes with DPP
-//    and v_permlane16_swap, entirely inside the wave: no LDS round trip and no barrier per
-//    token;
+//  - the kv and output sums over the 128 rows are reduced across the 32 lanes with four
+//    DPP steps and one ds_swizzle (lane ^ 16), entirely inside the wave: no LDS array and
+//    no barrier per token;
 //  - the inputs of 16 tokens (q/k rows of the key head, the block's v columns, e^{g},
 //    beta and k.q) are staged in double-buffered LDS; the next tile's global loads are in
 //    flight while the current tile computes; one barrier per 16 tokens.
