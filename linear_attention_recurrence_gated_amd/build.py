@@ -4,8 +4,8 @@
 
 Every source is compiled with hipcc for gfx950 with packed-FP32 VALU instructions
 disabled (`-Xclang -target-feature -Xclang -packed-fp32-ops`; hipcc's host pass warns that
-it does not know the feature, which is harmless), then linked into one shared library
-next to this file.
+it does not know the feature, which is harmless) and matrix-core results kept in VGPRs
+(`-mllvm -amdgpu-mfma-vgpr-form`), then linked into one shared library next to this file.
 """
 from __future__ import annotations
 
@@ -25,6 +25,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the state and the products are then used by
+    # vector instructions in place, with no accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

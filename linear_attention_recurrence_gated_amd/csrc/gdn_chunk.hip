@@ -25,6 +25,8 @@
 //    then D = T U, O = e^{gamma} Q S0 + P D and the rank-32 state update K^T D run as
 //    further 16x16x4 MFMAs.  K and Q of the next chunk are staged through double-buffered
 //    LDS while the current chunk computes.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -182,136 +184,167 @@ __device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, Pre
 // One workgroup = one value head x 32 value columns: 4 waves, wave (cs, rh) owning value
 // columns 16 cs .. 16 cs + 15 of the workgroup and key rows 64 rh .. 64 rh + 63.  Every
 // operand a chunk needs (K and Q rows of the key head, the head's WY slot from the
-// workspace and the workgroup's V tile) is staged into LDS once per workgroup with
-// coalesced 16-byte loads, one chunk ahead, and read from LDS by the waves; only the
-// outputs go straight to memory.
-constexpr int SC_NT = 256;  // threads per scan workgroup
-constexpr int SC_COLS = 32; // value columns per scan workgroup
-constexpr int TPAD = 36;    // LDS row stride of T, P and V^T (floats): conflict-free reads
+// workspace and the workgroup's V tile) is copied from global memory straight into LDS by
+// direct loads (16 bytes per lane, no registers, no LDS store instructions) into a ring of
+// three buffers, two chunks ahead (chunk c + 2 goes into the buffer of chunk c - 1 after
+// chunk c's barrier), and read from LDS by the waves; only the outputs go straight to
+// memory.
+constexpr int SC_NT = 256;   // threads per scan workgroup
+constexpr int SC_COLS = 32;  // value columns per scan workgroup
+constexpr int SC_RING = 3;   // chunk buffers in LDS
+
+// A direct load fills 64 consecutive 16-byte slots, so the tiles are unpadded; instead the
+// 16-byte columns of each row are permuted (XOR with a function of the row) so that the
+// reads below hit distinct LDS banks:
+//   K, Q  [32 tokens][32 float4]  float4 p of token t at t*32 + (p ^ (t & 15))
+//   T, P  [32 rows][8 float4]     float4 c of row i at i*8 + (c ^ sw8(i))
+//   V     [32 tokens][8 float4]   float4 c of token t at t*8 + (c ^ swv(t))
+//   misc  floats: e^gamma [0, 32), e^{gamma_last - gamma} [32, 64), e^{gamma_last} [64]
+__device__ __forceinline__ int sw8(int i) { return (i ^ (i >> 3)) & 7; }
+__device__ __forceinline__ int swv(int t) { return ((t >> 2) & 1) << 2; }
+
+struct ScanBuf {
+  f32x4 k[kChunk * 32];
+  f32x4 q[kChunk * 32];
+  f32x4 T[kChunk * 8];
+  f32x4 P[kChunk * 8];
+  f32x4 misc[64];
+  f32x4 v[kChunk * SC_COLS / 4];
+};
+
+constexpr int SC_XCHG = 2 * 2 * 2 * 3 * 64;  // [parity][col slice][row half][tile][lane]
 
 struct ScanSmem {
-  float k[2][kChunk][KP];
-  float q[2][kChunk][KP];
-  float T[2][kChunk][TPAD];        // T diag(beta)
-  float P[2][kChunk][TPAD];
-  float vt[2][SC_COLS][TPAD];      // V^T: [column of the workgroup][token]
-  float eg[2][kChunk], eb[2][kChunk], egl[2][4];
-  f32x4 x[2][2][2][4][64];         // exchange: [parity][col slice][row half][tile][lane]
+  ScanBuf buf[SC_RING];
+  f32x4 x[SC_XCHG];
 };
+static_assert(sizeof(ScanSmem) <= 160 * 1024, "LDS of one CU");
 
-// Global loads of one chunk's operands, held in registers until written to LDS.
-struct ScanStage {
-  f32x4 k[4], q[4];  // K/Q rows: float4 index tid + 256 i of the 32 x 32 float4 tile
-  f32x4 slot[3];     // workspace slot: float4 index tid + 256 i (< 544)
-  f32x4 v;           // V: token tid / 8, columns 4 (tid % 8) .. +3
-};
+// Raw buffer resource over `bytes` bytes from `base`; an empty range for bytes <= 0.
+__device__ __forceinline__ buf_rsrc rsrc_range(const float* base, int bytes) {
+  return make_rsrc(base, bytes > 0 ? (uint32_t)bytes : 0u);
+}
 
-// One scan workgroup (block index `b` of `nb` scan workgroups).
-__device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, ScanSmem& sm) {
-  constexpr int NCB = kDim / SC_COLS;  // column blocks per value head
-  constexpr int SLOT_F4 = kSlot / 4;   // 544
+template <int N>
+using ic = std::integral_constant<int, N>;
 
-  const int Hk = a.n_k_heads, Hv = a.n_v_heads, G = Hv / Hk;
-  const int L = xcd_grouped_block(b, nb);
-  // logical order: key head, then value head of the group, then column block
-  const int kh = L / (G * NCB), m = (L / NCB) % G, cblk = L % NCB;
-  const int h = kh + m * Hk;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int cs = w >> 1, rh = w & 1;
-  const int colw = 16 * cs + (l & 15);      // column inside the workgroup
+// One wave of a scan workgroup: row half RH (key rows 64 RH .. 64 RH + 63) of column slice
+// cs (value columns 16 cs .. 16 cs + 15 of the workgroup's 32).  The row half is a
+// template parameter and the chunk loop is unrolled over the three ring buffers, so every
+// LDS address is a loop-invariant per-lane base plus a constant, and the per-chunk global
+// offsets live in scalar buffer descriptors: the instructions between the matrix products
+// are the arithmetic of the method itself.
+template <int RH>
+__device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int cblk, int cs,
+                                          ScanSmem& sm) {
+  const int Hk = a.n_k_heads, Hv = a.n_v_heads;
+  const int l = threadIdx.x & 63, w = 2 * cs + RH;
+  const int q4 = l >> 4, lc = l & 15, lr = 4 * q4;
+  const int colw = 16 * cs + lc;            // column inside the workgroup
   const int col = cblk * SC_COLS + colw;    // value column
-  const int lr = 4 * (l >> 4);  // row offset of this lane inside a 16-row MFMA tile
   const int nch = (a.n_tok + kChunk - 1) / kChunk;
 
-  // state: tile rt holds rows 64 rh + 16 rt + lr + r, column col
+  // state: tile rt holds rows 64 RH + 16 rt + lr + r, column col
   f32x4 S[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      S[rt][r] = a.s_src[((size_t)h * kDim + 64 * rh + 16 * rt + lr + r) * kDim + col];
+      S[rt][r] = a.s_src[((size_t)h * kDim + 64 * RH + 16 * rt + lr + r) * kDim + col];
 
-  // The super-block's tokens, addressed through bounds-checked buffer resources: reads
-  // past its last token return 0 (the zero padding of a partial chunk), writes past it are
-  // dropped.  Byte offsets stay far below 2^32 (at most 2048 tokens per super-block).
-  const buf_rsrc rs_k = make_rsrc(a.k + (size_t)a.t_begin * Hk * kDim, a.n_tok * Hk * kDim * 4);
-  const buf_rsrc rs_q = make_rsrc(a.q + (size_t)a.t_begin * Hk * kDim, a.n_tok * Hk * kDim * 4);
-  const buf_rsrc rs_v = make_rsrc(a.v + (size_t)a.t_begin * Hv * kDim, a.n_tok * Hv * kDim * 4);
-  const buf_rsrc rs_o = make_rsrc(a.o + (size_t)a.t_begin * Hv * kDim, a.n_tok * Hv * kDim * 4);
-
-  ScanStage st;
-  // Global loads for chunk c (the workspace slot is clamped to the last chunk, so loads
-  // past the end stay inside the workspace; tokens past the end read as 0).  Every thread
-  // issues the same loads in every chunk, so the compiler's wait counts stay exact.
-  auto stage_load = [&](int c) {
+  // LDS element indices of this lane's reads, relative to a ring buffer; token tile tt
+  // and ring position add constants.
+  int ka_i[4];     // f32x4 in k / q: token lc, float4 16 RH + 4 rt + q4 of its row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + SC_NT * i, tt = f >> 5, p = f & 31;
-      const int off = (((c * kChunk + tt) * Hk + kh) * kDim + 4 * p) * 4;
-      st.k[i] = buf_load4(rs_k, off);
-      st.q[i] = buf_load4(rs_q, off);
+  for (int rt = 0; rt < 4; ++rt) ka_i[rt] = lc * 32 + ((16 * RH + 4 * rt + q4) ^ lc);
+  int kt_i[4][4];  // float in k: token lr + r, row 64 RH + 16 rt + lc
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = lr + r, row = 64 * RH + 16 * rt + lc;
+      kt_i[rt][r] = (t * 32 + ((row >> 2) ^ (t & 15))) * 4 + (row & 3);
     }
-    const f32x4* slot =
-        reinterpret_cast<const f32x4*>(a.ws + ((size_t)min(c, nch - 1) * Hv + h) * kSlot);
+  const int t00_i = lc * 8 + (q4 ^ sw8(lc));
+  const int t10_i = (16 + lc) * 8 + (q4 ^ sw8(16 + lc));
+  const int t11_i = (16 + lc) * 8 + ((4 + q4) ^ sw8(16 + lc));
+  const int pa_i = RH ? t10_i : t00_i;      // P tile (RH, 0)
+  // float in v: token lr (+ r, + 16 tt), column colw
+  const int vv_i = (lr * 8 + ((colw >> 2) ^ ((q4 & 1) << 2))) * 4 + (colw & 3);
+  const int xw_i = (cs * 2 + RH) * 3 * 64 + l;  // exchange: this wave's tiles
+  const int xr_i = cs * 2 * 3 * 64 + l;         // exchange: row half 0 of the column slice
+
+  // Per-lane byte offsets of this wave's 12 direct loads, relative to the chunk (K, Q, V)
+  // or to the workspace slot (T, P, decays).  Slot s of a 64-slot slice is lane s % 64.
+  uint32_t dk_off[4];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) st.slot[i] = slot[min(tid + SC_NT * i, SLOT_F4 - 1)];
-    st.v = buf_load4(rs_v, (((c * kChunk + (tid >> 3)) * Hv + h) * kDim + cblk * SC_COLS +
-                            4 * (tid & 7)) * 4);
+  for (int i = 0; i < 4; ++i) {
+    const int sl = 64 * (w + 4 * i) + l, t = sl >> 5, p = (l & 31) ^ (t & 15);
+    dk_off[i] = ((t * Hk + kh) * kDim + 4 * p) * 4;
+  }
+  const int srow = (64 * w + l) >> 3;
+  const uint32_t dt_off = (kSlotT + srow * kChunk + 4 * ((l & 7) ^ sw8(srow))) * 4;
+  const uint32_t dp_off = dt_off + (kSlotP - kSlotT) * 4;
+  const uint32_t dm_off = (kSlotEg + 4 * min(l, 16)) * 4;  // lanes past 16 repeat lane 16
+  const uint32_t dv_off = ((srow * Hv + h) * kDim + cblk * SC_COLS + 4 * ((l & 7) ^ swv(srow))) * 4;
+  // O stores of token 16 RH + lr + r of a chunk
+  uint32_t o_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o_off[r] = (((16 * RH + lr + r) * Hv + h) * kDim + col) * 4;
+
+  // Descriptors of chunk c: its tokens onward (an empty range past the end, so loads
+  // return 0 and stores are dropped) and its workspace slot (clamped to the last chunk).
+  auto tok_rsrc = [&](const float* base, int row_floats, int c) {
+    return rsrc_range(base + (size_t)(a.t_begin + c * kChunk) * row_floats,
+                      (a.n_tok - c * kChunk) * row_floats * 4);
   };
-  auto stage_store = [&](int b) {
+  auto issue = [&](auto rbc, int c) {  // direct loads of chunk c into ring buffer rbc
+    ScanBuf& B = sm.buf[decltype(rbc)::value];
+    const buf_rsrc rk = tok_rsrc(a.k, Hk * kDim, c), rq = tok_rsrc(a.q, Hk * kDim, c);
+    const buf_rsrc rv = tok_rsrc(a.v, Hv * kDim, c);
+    const buf_rsrc rw = make_rsrc(a.ws + ((size_t)min(c, nch - 1) * Hv + h) * kSlot, kSlot * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + SC_NT * i, tt = f >> 5, p = f & 31;
-      *reinterpret_cast<f32x4*>(&sm.k[b][tt][4 * p]) = st.k[i];
-      *reinterpret_cast<f32x4*>(&sm.q[b][tt][4 * p]) = st.q[i];
-    }
-    // slot float4 f: T rows (f < 256), P rows (f < 512), then e^gamma, e^(last-gamma), e^last
-    *reinterpret_cast<f32x4*>(&sm.T[b][tid >> 3][4 * (tid & 7)]) = st.slot[0];
-    *reinterpret_cast<f32x4*>(&sm.P[b][tid >> 3][4 * (tid & 7)]) = st.slot[1];
-    if (tid < 8) *reinterpret_cast<f32x4*>(&sm.eg[b][4 * tid]) = st.slot[2];
-    else if (tid < 16) *reinterpret_cast<f32x4*>(&sm.eb[b][4 * (tid - 8)]) = st.slot[2];
-    else if (tid == 16) *reinterpret_cast<f32x4*>(&sm.egl[b][0]) = st.slot[2];
-    const int vt_tok = tid >> 3, vt_col = 4 * (tid & 7);
+    for (int i = 0; i < 4; ++i) buf_load_lds16(rk, dk_off[i], &B.k[64 * (w + 4 * i)]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.vt[b][vt_col + i][vt_tok] = st.v[i];
+    for (int i = 0; i < 4; ++i) buf_load_lds16(rq, dk_off[i], &B.q[64 * (w + 4 * i)]);
+    buf_load_lds16(rw, dt_off, &B.T[64 * w]);
+    buf_load_lds16(rw, dp_off, &B.P[64 * w]);
+    buf_load_lds16(rw, dm_off, &B.misc[0]);
+    buf_load_lds16(rv, dv_off, &B.v[64 * w]);
   };
 
-  auto chunk_step = [&](int c) {
-    const int buf = c & 1;
-    // (a) operands of this chunk from LDS (written before the previous chunk's barrier),
-    //     then partial K S0 and Q S0 over this wave's 64 rows.
+  auto step = [&](auto rbc, int c) {
+    constexpr int RB = decltype(rbc)::value, RB2 = (RB + 2) % SC_RING;
+    const ScanBuf& B = sm.buf[RB];
+    const float* kf = reinterpret_cast<const float*>(B.k);
+    const float* vf = reinterpret_cast<const float*>(B.v);
+
+    // (a) This chunk's operands (loaded and published before the previous barrier).
     f32x4 ka[4][2], qa[4][2];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int row = 64 * rh + 16 * rt + lr;
-        ka[rt][tt] = *reinterpret_cast<const f32x4*>(&sm.k[buf][16 * tt + (l & 15)][row]);
-        qa[rt][tt] = *reinterpret_cast<const f32x4*>(&sm.q[buf][16 * tt + (l & 15)][row]);
-      }
     float kt[4][2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt) {
+        ka[rt][tt] = B.k[ka_i[rt] + 16 * 32 * tt];
+        qa[rt][tt] = B.q[ka_i[rt] + 16 * 32 * tt];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          kt[rt][tt][r] = sm.k[buf][16 * tt + lr + r][64 * rh + 16 * rt + (l & 15)];
-    const int ar = l & 15;
-    const f32x4 T00 = *reinterpret_cast<const f32x4*>(&sm.T[buf][ar][lr]);
-    const f32x4 T10 = *reinterpret_cast<const f32x4*>(&sm.T[buf][16 + ar][lr]);
-    const f32x4 T11 = *reinterpret_cast<const f32x4*>(&sm.T[buf][16 + ar][16 + lr]);
-    const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sm.P[buf][16 * rh + ar][lr]);
-    const f32x4 Pb = *reinterpret_cast<const f32x4*>(&sm.P[buf][16 + ar][16 + lr]);
+        for (int r = 0; r < 4; ++r) kt[rt][tt][r] = kf[kt_i[rt][r] + 16 * 32 * 4 * tt];
+      }
+    const f32x4 T00 = B.T[t00_i], T10 = B.T[t10_i], T11 = B.T[t11_i];
+    const f32x4 Pa = B.P[pa_i], Pb = B.P[t11_i];
     f32x4 eg[2], eb[2], vv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      eg[tt] = *reinterpret_cast<const f32x4*>(&sm.eg[buf][16 * tt + lr]);
-      eb[tt] = *reinterpret_cast<const f32x4*>(&sm.eb[buf][16 * tt + lr]);
-      vv[tt] = *reinterpret_cast<const f32x4*>(&sm.vt[buf][colw][16 * tt + lr]);
+      eg[tt] = B.misc[4 * tt + q4];
+      eb[tt] = B.misc[8 + 4 * tt + q4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vv[tt][r] = vf[vv_i + 32 * r + 16 * 32 * tt];
     }
-    const float egl = sm.egl[buf][0];
+    const float egl = reinterpret_cast<const float*>(B.misc)[64];
 
+    // (b) Partial K S0 and Q S0 over this wave's 64 rows; the state registers are the B
+    //     operand as they are.
     f32x4 P4[4];  // partial W0, W1, QS0, QS1
 #pragma unroll
     for (int i = 0; i < 4; ++i) P4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -325,32 +358,30 @@ __device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, Sc
           P4[2 + tt] = mfma16x16x4(qa[rt][tt][r], S[rt][r], P4[2 + tt]);
         }
 
-    // (a') stage chunk c+1 into the other LDS buffer (its last reads were in chunk c-1's
-    //      phase (a), before that chunk's barrier), then load chunk c+2.
-    stage_store(buf ^ 1);
-    stage_load(c + 2);
-
-    // (b) exchange partial sums with the other row half of the same columns; both halves
-    //     add the two halves in the same order, so they hold identical sums.
-    const int par = c & 1;
-    sm.x[par][cs][rh][0][l] = P4[0];
-    sm.x[par][cs][rh][1][l] = P4[1];
-    sm.x[par][cs][rh][2][l] = rh ? P4[2] : P4[3];  // the other half's output tile
-    __syncthreads();
+    // (c) Exchange with the other row half of the same columns: both W partials and the
+    //     Q S0 partial of the other half's output tile.  Publish it together with the
+    //     direct loads of chunk c + 1 (the last memory operations before this point).
+    const int xo = (c & 1) * (SC_XCHG / 2);
+    sm.x[xo + xw_i] = P4[0];
+    sm.x[xo + xw_i + 64] = P4[1];
+    sm.x[xo + xw_i + 128] = RH ? P4[2] : P4[3];
+    wait_vm_lgkm0<0>();
+    barrier_only();
+    // Both halves add the two partials in the same order, so they hold identical sums.
     f32x4 W[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) W[tt] = sm.x[par][cs][0][tt][l] + sm.x[par][cs][1][tt][l];
-    const f32x4 QSo = sm.x[par][cs][1 - rh][2][l];
-    const f32x4 QSf = rh ? (QSo + P4[3]) : (P4[2] + QSo);
+    for (int tt = 0; tt < 2; ++tt) W[tt] = sm.x[xo + xr_i + 64 * tt] + sm.x[xo + xr_i + 192 + 64 * tt];
+    const f32x4 QSo = sm.x[xo + xr_i + 192 * (1 - RH) + 128];
+    const f32x4 QSf = RH ? (QSo + P4[3]) : (P4[2] + QSo);
 
-    // (c) U = V - e^{gamma} (K S0), C layout: token 16 tt + lr + r, column col.
+    // (d) U = V - e^{gamma} (K S0), C layout: token 16 tt + lr + r, column col.
     f32x4 U[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) U[tt][r] = fmaf(-eg[tt][r], W[tt][r], vv[tt][r]);
 
-    // (d) D = T diag(beta) U; T is lower triangular, so tile (0,1) is zero.
+    // (e) D = T diag(beta) U; T is lower triangular, so tile (0,1) is zero.
     f32x4 D[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -360,45 +391,75 @@ __device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, Sc
 #pragma unroll
     for (int r = 0; r < 4; ++r) D[1] = mfma16x16x4(T11[r], U[1][r], D[1]);
 
-    // (e) outputs of token tile rh: O = e^{gamma} Q S0 + P D (P lower triangular).
-    f32x4 O = (rh ? eg[1] : eg[0]) * QSf;
+    // (f) Outputs of token tile RH: O = e^{gamma} Q S0 + P D (P lower triangular).
+    f32x4 O = eg[RH] * QSf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) O = mfma16x16x4(Pa[r], D[0][r], O);
-    if (rh == 1) {
+    if (RH == 1) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) O = mfma16x16x4(Pb[r], D[1][r], O);
     }
+    const buf_rsrc ro = tok_rsrc(a.o, Hv * kDim, c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {  // dropped by the buffer past the last token
-      const int tk = c * kChunk + 16 * rh + lr + r;
-      buf_store(rs_o, ((tk * Hv + h) * kDim + col) * 4, O[r]);
-    }
+    for (int r = 0; r < 4; ++r) buf_store(ro, o_off[r], O[r]);  // dropped past the end
 
-    // (f, g) S' = e^{gamma_last} S0 + K^T diag(e^{gamma_last - gamma}) D.
+    // (g) S' = e^{gamma_last} S0 + K^T diag(e^{gamma_last - gamma}) D, with the direct
+    //     loads of chunk c + 2 spread between the products (into the buffer of chunk
+    //     c - 1, which every wave read before the previous barrier).
     f32x4 Dh[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) Dh[tt] = eb[tt] * D[tt];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) S[rt] = egl * S[rt];
+    issue(ic<RB2>(), c + 2);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) S[rt] = mfma16x16x4(kt[rt][tt][r], Dh[tt][r], S[rt]);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 vector memory load
+    }
   };
 
-  stage_load(0);
-  stage_store(0);
-  stage_load(1);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) chunk_step(c);
+  issue(ic<0>(), 0);
+  issue(ic<1>(), 1);
+  wait_vm_lgkm0<0>();
+  barrier_only();
+  for (int c = 0; c < nch; c += SC_RING) {
+    step(ic<0>(), c);
+    if (c + 1 >= nch) break;
+    step(ic<1>(), c + 1);
+    if (c + 2 >= nch) break;
+    step(ic<2>(), c + 2);
+  }
+  // The direct loads past the last chunk (never read) must land before the workgroup's
+  // LDS is released.
+  wait_vm_lgkm0<0>();
 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      a.s_dst[((size_t)h * kDim + 64 * rh + 16 * rt + lr + r) * kDim + col] = S[rt][r];
+      a.s_dst[((size_t)h * kDim + 64 * RH + 16 * rt + lr + r) * kDim + col] = S[rt][r];
+}
+
+// One scan workgroup (block index `b` of `nb` scan workgroups).
+__device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, ScanSmem& sm) {
+  constexpr int NCB = kDim / SC_COLS;  // column blocks per value head
+  const int Hk = a.n_k_heads, G = a.n_v_heads / Hk;
+  const int L = xcd_grouped_block(b, nb);
+  // logical order: key head, then value head of the group, then column block
+  const int kh = L / (G * NCB), m = (L / NCB) % G, cblk = L % NCB;
+  const int h = kh + m * Hk;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w & 1)
+    scan_wave<1>(a, h, kh, cblk, w >> 1, sm);
+  else
+    scan_wave<0>(a, h, kh, cblk, w >> 1, sm);
 }
 
 // Prep alone: one workgroup per (chunk, key head) of a super-block.

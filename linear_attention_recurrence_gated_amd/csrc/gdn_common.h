@@ -67,6 +67,32 @@ __device__ __forceinline__ void buf_store(buf_rsrc r, uint32_t byte_off, float v
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
 
+// Direct global -> LDS load (gfx950): lane l's 16 bytes at byte_off land at
+// lds_base + 16 l, without passing through registers.  lds_base must be the same for the
+// whole wave.  Counted by vmcnt like any vector memory load; nothing waits for it
+// implicitly, so the caller waits (wait_vm) before a barrier that publishes the data.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ __forceinline__ void buf_load_lds16(buf_rsrc r, uint32_t byte_off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 16, byte_off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector memory operations of this wave remain
+// in flight (they complete in issue order) and all its LDS operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without the implicit waits of __syncthreads (the caller has waited for
+// exactly what the other waves will read); the empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).  This
 // maps a workgroup id to a logical block so that consecutive logical blocks share an XCD
 // (and its L2): XCD x receives the logical range [x*n/8, (x+1)*n/8).
