@@ -25,6 +25,7 @@
 //    then D = T U, O = e^{gamma} Q S0 + P D and the rank-32 state update K^T D run as
 //    further 16x16x4 MFMAs.  K and Q of the next chunk are staged through double-buffered
 //    LDS while the current chunk computes.
+#include <cstddef>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -51,11 +52,12 @@ struct PrepSmem {
 };
 
 // The operators of chunk c for key head kh and its value heads.  Called by every thread
-// of a 256-thread workgroup (it contains barriers); ends with a barrier, so one
-// workgroup may process several items in a row.
-__device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, PrepSmem& sm) {
+// of a group of 256 threads (thread `tid` of the group; it contains workgroup barriers,
+// which every group of the workgroup reaches the same number of times per item); ends with
+// a barrier, so a group may process several items in a row.
+__device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, PrepSmem& sm, int tid) {
   const int Hk = a.n_k_heads, Hv = a.n_v_heads, G = Hv / Hk;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int w = tid >> 6, l = tid & 63;
   const int c0 = c * kChunk;  // first token of the chunk, relative to the super-block
 
   // 1. K, Q rows of the chunk (zero past the end), g and beta of the value heads.
@@ -181,15 +183,16 @@ __device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, Pre
 // ---------------------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------------------
-// One workgroup = one value head x 32 value columns: 4 waves, wave (cs, rh) owning value
-// columns 16 cs .. 16 cs + 15 of the workgroup and key rows 64 rh .. 64 rh + 63.  Every
-// operand a chunk needs (K and Q rows of the key head, the head's WY slot from the
-// workspace and the workgroup's V tile) is copied from global memory straight into LDS by
-// direct loads (16 bytes per lane, no registers, no LDS store instructions) into a ring of
-// three buffers, two chunks ahead (chunk c + 2 goes into the buffer of chunk c - 1 after
-// chunk c's barrier), and read from LDS by the waves; only the outputs go straight to
-// memory.
-constexpr int SC_NT = 256;   // threads per scan workgroup
+// One workgroup = one value head x 32 value columns: 4 compute waves, wave (cs, rh) owning
+// value columns 16 cs .. 16 cs + 15 of the workgroup and key rows 64 rh .. 64 rh + 63, and
+// a producer wave.  Every operand a chunk needs (K and Q rows of the key head, the head's
+// WY slot from the workspace and the workgroup's V tile) is copied by the producer from
+// global memory straight into LDS with direct loads (16 bytes per lane, no registers, no
+// LDS store instructions), into a ring of three buffers, chunk c + 3 into the buffer of
+// chunk c as soon as chunk c's barrier has passed; the compute waves read everything from
+// LDS and issue no loads (a direct load holds its wave for as long as the CU's vector
+// memory path needs to move its 1 KB), only their output stores.
+constexpr int SC_NT = 320;   // threads per scan workgroup: 4 compute waves + 1 producer
 constexpr int SC_COLS = 32;  // value columns per scan workgroup
 constexpr int SC_RING = 3;   // chunk buffers in LDS
 
@@ -237,8 +240,8 @@ using ic = std::integral_constant<int, N>;
 template <int RH>
 __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int cblk, int cs,
                                           ScanSmem& sm) {
-  const int Hk = a.n_k_heads, Hv = a.n_v_heads;
-  const int l = threadIdx.x & 63, w = 2 * cs + RH;
+  const int Hv = a.n_v_heads;
+  const int l = threadIdx.x & 63;
   const int q4 = l >> 4, lc = l & 15, lr = 4 * q4;
   const int colw = 16 * cs + lc;            // column inside the workgroup
   const int col = cblk * SC_COLS + colw;    // value column
@@ -274,19 +277,6 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
   const int xw_i = (cs * 2 + RH) * 3 * 64 + l;  // exchange: this wave's tiles
   const int xr_i = cs * 2 * 3 * 64 + l;         // exchange: row half 0 of the column slice
 
-  // Per-lane byte offsets of this wave's 12 direct loads, relative to the chunk (K, Q, V)
-  // or to the workspace slot (T, P, decays).  Slot s of a 64-slot slice is lane s % 64.
-  uint32_t dk_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sl = 64 * (w + 4 * i) + l, t = sl >> 5, p = (l & 31) ^ (t & 15);
-    dk_off[i] = ((t * Hk + kh) * kDim + 4 * p) * 4;
-  }
-  const int srow = (64 * w + l) >> 3;
-  const uint32_t dt_off = (kSlotT + srow * kChunk + 4 * ((l & 7) ^ sw8(srow))) * 4;
-  const uint32_t dp_off = dt_off + (kSlotP - kSlotT) * 4;
-  const uint32_t dm_off = (kSlotEg + 4 * min(l, 16)) * 4;  // lanes past 16 repeat lane 16
-  const uint32_t dv_off = ((srow * Hv + h) * kDim + cblk * SC_COLS + 4 * ((l & 7) ^ swv(srow))) * 4;
   // O stores of token 16 RH + lr + r of a chunk
   uint32_t o_off[4];
 #pragma unroll
@@ -298,23 +288,8 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     return rsrc_range(base + (size_t)(a.t_begin + c * kChunk) * row_floats,
                       (a.n_tok - c * kChunk) * row_floats * 4);
   };
-  auto issue = [&](auto rbc, int c) {  // direct loads of chunk c into ring buffer rbc
-    ScanBuf& B = sm.buf[decltype(rbc)::value];
-    const buf_rsrc rk = tok_rsrc(a.k, Hk * kDim, c), rq = tok_rsrc(a.q, Hk * kDim, c);
-    const buf_rsrc rv = tok_rsrc(a.v, Hv * kDim, c);
-    const buf_rsrc rw = make_rsrc(a.ws + ((size_t)min(c, nch - 1) * Hv + h) * kSlot, kSlot * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buf_load_lds16(rk, dk_off[i], &B.k[64 * (w + 4 * i)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buf_load_lds16(rq, dk_off[i], &B.q[64 * (w + 4 * i)]);
-    buf_load_lds16(rw, dt_off, &B.T[64 * w]);
-    buf_load_lds16(rw, dp_off, &B.P[64 * w]);
-    buf_load_lds16(rw, dm_off, &B.misc[0]);
-    buf_load_lds16(rv, dv_off, &B.v[64 * w]);
-  };
-
   auto step = [&](auto rbc, int c) {
-    constexpr int RB = decltype(rbc)::value, RB2 = (RB + 2) % SC_RING;
+    constexpr int RB = decltype(rbc)::value;
     const ScanBuf& B = sm.buf[RB];
     const float* kf = reinterpret_cast<const float*>(B.k);
     const float* vf = reinterpret_cast<const float*>(B.v);
@@ -359,13 +334,13 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
         }
 
     // (c) Exchange with the other row half of the same columns: both W partials and the
-    //     Q S0 partial of the other half's output tile.  Publish it together with the
-    //     direct loads of chunk c + 1 (the last memory operations before this point).
+    //     Q S0 partial of the other half's output tile.  (The producer has published
+    //     chunk c + 1 by the same barrier.)
     const int xo = (c & 1) * (SC_XCHG / 2);
     sm.x[xo + xw_i] = P4[0];
     sm.x[xo + xw_i + 64] = P4[1];
     sm.x[xo + xw_i + 128] = RH ? P4[2] : P4[3];
-    wait_vm_lgkm0<0>();
+    wait_vm_lgkm0<63>();  // LDS writes done; the O stores may still be in flight
     barrier_only();
     // Both halves add the two partials in the same order, so they hold identical sums.
     f32x4 W[2];
@@ -403,32 +378,21 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
 #pragma unroll
     for (int r = 0; r < 4; ++r) buf_store(ro, o_off[r], O[r]);  // dropped past the end
 
-    // (g) S' = e^{gamma_last} S0 + K^T diag(e^{gamma_last - gamma}) D, with the direct
-    //     loads of chunk c + 2 spread between the products (into the buffer of chunk
-    //     c - 1, which every wave read before the previous barrier).
+    // (g) S' = e^{gamma_last} S0 + K^T diag(e^{gamma_last - gamma}) D.
     f32x4 Dh[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) Dh[tt] = eb[tt] * D[tt];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) S[rt] = egl * S[rt];
-    issue(ic<RB2>(), c + 2);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) S[rt] = mfma16x16x4(kt[rt][tt][r], Dh[tt][r], S[rt]);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 vector memory load
-    }
   };
 
-  issue(ic<0>(), 0);
-  issue(ic<1>(), 1);
-  wait_vm_lgkm0<0>();
-  barrier_only();
+  barrier_only();  // chunk 0 published by the producer
   for (int c = 0; c < nch; c += SC_RING) {
     step(ic<0>(), c);
     if (c + 1 >= nch) break;
@@ -436,15 +400,89 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     if (c + 2 >= nch) break;
     step(ic<2>(), c + 2);
   }
-  // The direct loads past the last chunk (never read) must land before the workgroup's
-  // LDS is released.
-  wait_vm_lgkm0<0>();
 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       a.s_dst[((size_t)h * kDim + 64 * RH + 16 * rt + lr + r) * kDim + col] = S[rt][r];
+}
+
+// The producer wave of a scan workgroup: all direct loads of every chunk, and the waits
+// that make a chunk's operands complete before the barrier that publishes them.  It meets
+// the compute waves at the same barriers (one before the first chunk, one per chunk).
+constexpr int SC_DMA = 45;  // direct loads per chunk: K 16, Q 16, T 4, P 4, decays 1, V 4
+
+__device__ __forceinline__ void scan_producer(const ChunkArgs& a, int h, int kh, int cblk,
+                                              ScanSmem& sm) {
+  const int Hk = a.n_k_heads, Hv = a.n_v_heads;
+  const int l = threadIdx.x & 63;
+  const int nch = (a.n_tok + kChunk - 1) / kChunk;
+
+  // Per-lane byte offsets: slot s of a 64-slot slice is lane s % 64, so each lane fetches
+  // the source float4 that the permutation of the tile puts there.  K and Q slices
+  // relative to the chunk's first token, T / P / decays relative to the workspace slot, V
+  // relative to the chunk's first token.
+  uint32_t off_kq[16], off_t[4], off_p[4], off_v[4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = (64 * i + l) >> 5, p = (l & 31) ^ (t & 15);
+    off_kq[i] = ((t * Hk + kh) * kDim + 4 * p) * 4;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int srow = (64 * i + l) >> 3;
+    off_t[i] = (kSlotT + srow * kChunk + 4 * ((l & 7) ^ sw8(srow))) * 4;
+    off_p[i] = off_t[i] + (kSlotP - kSlotT) * 4;
+    off_v[i] = ((srow * Hv + h) * kDim + cblk * SC_COLS + 4 * ((l & 7) ^ swv(srow))) * 4;
+  }
+  const uint32_t off_m = (kSlotEg + 4 * min(l, 16)) * 4;  // lanes past 16 repeat lane 16
+  const uint32_t lds = lds_address(&sm);
+
+  // Descriptors of chunk c: its tokens onward (an empty range past the end, so the loads
+  // return 0) and its workspace slot (clamped to the last chunk).
+  auto tok_desc = [&](const float* base, int row_floats, int c) {
+    return make_desc(base + (size_t)(a.t_begin + c * kChunk) * row_floats,
+                     (a.n_tok - c * kChunk) * row_floats * 4);
+  };
+  auto issue = [&](auto rbc, int c) {
+    constexpr int B0 = offsetof(ScanSmem, buf) + decltype(rbc)::value * (int)sizeof(ScanBuf);
+    const i32x4 dk = tok_desc(a.k, Hk * kDim, c), dq = tok_desc(a.q, Hk * kDim, c);
+    const i32x4 dv = tok_desc(a.v, Hv * kDim, c);
+    const i32x4 dw = make_desc(a.ws + ((size_t)min(c, nch - 1) * Hv + h) * kSlot, kSlot * 4);
+    const auto s16 = std::make_integer_sequence<int, 16>();
+    const auto s4 = std::make_integer_sequence<int, 4>();
+    dma16_run<B0 + offsetof(ScanBuf, k)>(dk, off_kq, lds, s16);
+    dma16_run<B0 + offsetof(ScanBuf, q)>(dq, off_kq, lds, s16);
+    dma16_run<B0 + offsetof(ScanBuf, T)>(dw, off_t, lds, s4);
+    dma16_run<B0 + offsetof(ScanBuf, P)>(dw, off_p, lds, s4);
+    dma16_run<B0 + offsetof(ScanBuf, v)>(dv, off_v, lds, s4);
+    dma16<B0 + offsetof(ScanBuf, misc)>(dw, off_m, lds);
+  };
+  // At the barrier of chunk c the loads of chunk c + 1 must have landed; those of chunk
+  // c + 2 (issued after the previous barrier) may still be in flight.  After it, every
+  // compute wave has read chunk c, whose buffer then takes chunk c + 3.
+  auto publish = [&]() {
+    wait_vm_lgkm0<SC_DMA>();
+    barrier_only();
+  };
+  issue(ic<0>(), 0);
+  issue(ic<1>(), 1);
+  publish();
+  issue(ic<2>(), 2);
+  for (int c = 0; c < nch; c += SC_RING) {
+    publish();
+    issue(ic<0>(), c + 3);
+    if (c + 1 >= nch) break;
+    publish();
+    issue(ic<1>(), c + 4);
+    if (c + 2 >= nch) break;
+    publish();
+    issue(ic<2>(), c + 5);
+  }
+  // Loads past the last chunk (never read) must land before the workgroup's LDS is
+  // released.
+  wait_vm_lgkm0<0>();
 }
 
 // One scan workgroup (block index `b` of `nb` scan workgroups).
@@ -456,7 +494,9 @@ __device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, Sc
   const int kh = L / (G * NCB), m = (L / NCB) % G, cblk = L % NCB;
   const int h = kh + m * Hk;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w & 1)
+  if (w == 4)
+    scan_producer(a, h, kh, cblk, sm);
+  else if (w & 1)
     scan_wave<1>(a, h, kh, cblk, w >> 1, sm);
   else
     scan_wave<0>(a, h, kh, cblk, w >> 1, sm);
@@ -465,7 +505,7 @@ __device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, Sc
 // Prep alone: one workgroup per (chunk, key head) of a super-block.
 __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(ChunkArgs a) {
   __shared__ PrepSmem sm;
-  prep_item(a, blockIdx.x, blockIdx.y, sm);
+  prep_item(a, blockIdx.x, blockIdx.y, sm, threadIdx.x);
 }
 
 // Scan of super-block n fused with the prep of super-block n+1: workgroups
@@ -482,20 +522,28 @@ struct FusedArgs {
 
 union FusedSmem {
   ScanSmem scan;
-  PrepSmem prep;
+  PrepSmem prep[2];  // one per group of 4 waves
 };
 
-__global__ __launch_bounds__(SC_NT) void chunk_fused_kernel(FusedArgs f) {
-  static_assert(SC_NT == PREP_NT, "both roles run with the same workgroup size");
+// Workgroups of 512 threads (8 waves, two per SIMD).  A scan workgroup uses 4 compute waves
+// and the producer (the other 3 end at once); a prep workgroup runs two independent streams
+// of items, waves 0-3 and 4-7, each with its own LDS area (a wave that has ended no longer
+// takes part in barriers, so a stream that runs out of items simply ends).
+constexpr int FUSED_NT = 512;
+static_assert(FUSED_NT >= SC_NT && FUSED_NT == 2 * PREP_NT, "roles of the fused workgroup");
+
+__global__ __launch_bounds__(FUSED_NT) void chunk_fused_kernel(FusedArgs f) {
   __shared__ FusedSmem sm;
   const int b = blockIdx.x;
   if (b < f.n_scan) {
-    scan_block(f.scan, b, f.n_scan, sm.scan);
+    if (threadIdx.x < SC_NT) scan_block(f.scan, b, f.n_scan, sm.scan);
   } else if (f.has_prep) {
     const int Hk = f.prep.n_k_heads;
     const int items = ((f.prep.n_tok + kChunk - 1) / kChunk) * Hk;
-    const int n_prep = gridDim.x - f.n_scan;
-    for (int it = b - f.n_scan; it < items; it += n_prep) prep_item(f.prep, it / Hk, it % Hk, sm.prep);
+    const int n_streams = 2 * ((int)gridDim.x - f.n_scan);
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / PREP_NT);
+    for (int it = 2 * (b - f.n_scan) + g; it < items; it += n_streams)
+      prep_item(f.prep, it / Hk, it % Hk, sm.prep[g], threadIdx.x - g * PREP_NT);
   }
 }
 
@@ -523,7 +571,7 @@ hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_
   }
   void* args[] = {&f};
   return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_fused_kernel),
-                         dim3(f.n_scan + n_prep), dim3(SC_NT), args, 0, stream);
+                         dim3(f.n_scan + n_prep), dim3(FUSED_NT), args, 0, stream);
 }
 
 }  // namespace gdn

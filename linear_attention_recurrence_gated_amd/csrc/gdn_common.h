@@ -2,6 +2,8 @@
 // FP32 matrix-core product and the XCD-aware block order.
 #pragma once
 
+#include <utility>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,13 +69,33 @@ __device__ __forceinline__ void buf_store(buf_rsrc r, uint32_t byte_off, float v
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
 
-// Direct global -> LDS load (gfx950): lane l's 16 bytes at byte_off land at
-// lds_base + 16 l, without passing through registers.  lds_base must be the same for the
-// whole wave.  Counted by vmcnt like any vector memory load; nothing waits for it
-// implicitly, so the caller waits (wait_vm) before a barrier that publishes the data.
-typedef __attribute__((address_space(3))) void* lds_ptr;
-__device__ __forceinline__ void buf_load_lds16(buf_rsrc r, uint32_t byte_off, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 16, byte_off, 0, 0, 0);
+// Direct global -> LDS load (gfx950): lane l's 16 bytes at byte_off (from the descriptor's
+// base, checked against its size: out of range reads as 0) land at LDS address
+// lds_base + LDS_OFF + 16 l, without passing through registers.  The wave-uniform LDS
+// address travels in m0, which nothing else in these kernels uses.  Issued as inline
+// assembly so that the compiler does not treat it as a pending LDS write (it would then
+// wait for every such load before the next LDS read); the caller waits with wait_vm_lgkm0
+// before the barrier that publishes the data.  LDS_OFF is an immediate, so an unrolled run
+// of loads keeps one base register rather than one per destination.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char* lds_cptr;
+__device__ __forceinline__ i32x4 make_desc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), bytes > 0 ? bytes : 0, kBufferDword3};
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(size_t)(lds_cptr)p;
+}
+template <int LDS_OFF>
+__device__ __forceinline__ void dma16(const i32x4& desc, uint32_t byte_off, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               :: "s"(lds_base), "i"(LDS_OFF), "v"(byte_off), "s"(desc) : "scc");
+}
+// Loads I = 0, 1, ... of a run: destination LDS_OFF + 1024 I, per-lane offsets off[I].
+template <int LDS_OFF, int... I>
+__device__ __forceinline__ void dma16_run(const i32x4& desc, const uint32_t* off, uint32_t lds_base,
+                                          std::integer_sequence<int, I...>) {
+  (dma16<LDS_OFF + 1024 * I>(desc, off[I], lds_base), ...);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector memory operations of this wave remain
