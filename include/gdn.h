@@ -145,6 +145,43 @@ int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
 int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint16_t* y,
                  int64_t T, int n_v_heads, int dv, void* stream);
 
+/*
+ * One layer's prompt path: the chunked recurrence (gdn_recurrence_chunked, same
+ * arguments, same results bit for bit) followed by the gated RMS output norm
+ * (gdn_out_norm with z, w, eps, y, same results bit for bit), in one call.  The norm of
+ * each 2048-token super-block runs inside the recurrence launch of the next super-block,
+ * on waves the scan leaves free, so it costs next to nothing; only the last super-block's
+ * norm is a launch of its own.  The FP32 output o is still written (it is the norm's
+ * input and a result of the call).
+ *
+ * ("#1372 DeltaNet recurrence: STRATA_GDN_CHUNKED=1", section "What it does", for the
+ * recurrence; "#413 ...", section "What changes", for the norm, which the pages keep as a
+ * separate kernel after the recurrence: running it inside the next recurrence launch is
+ * this library's arrangement.)
+ *
+ *   z, w, eps, y : as for gdn_out_norm.  y must not overlap any other argument; o, the
+ *                  state and the workspace must not overlap z or w.
+ *   Everything else as for gdn_recurrence_chunked.  T = 0 copies the state and writes
+ *   nothing else.
+ */
+int gdn_layer_chunked(const float* q, const float* k, const float* v, const float* g,
+                      const float* beta, const float* state_in, float* state_out, float* o,
+                      const float* z, const float* w, float eps, uint16_t* y, int64_t T,
+                      int n_k_heads, int n_v_heads, int dk, int dv, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_layer_chunked that additionally records caller-created hipEvent_t handles around
+ * each recurrence launch (the launch of super-block sb between scan_events[2 sb] and
+ * scan_events[2 sb + 1], for 2 sb + 1 < n_scan_events), on `stream`.  For timing.
+ */
+int gdn_layer_chunked_timed(const float* q, const float* k, const float* v, const float* g,
+                            const float* beta, const float* state_in, float* state_out,
+                            float* o, const float* z, const float* w, float eps, uint16_t* y,
+                            int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                            void* workspace, size_t workspace_bytes,
+                            void* const* scan_events, int n_scan_events, void* stream);
+
 /* A static, never-NULL description of a gdn_status value. */
 const char* gdn_status_string(int status);
 

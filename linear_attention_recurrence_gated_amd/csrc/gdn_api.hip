@@ -79,6 +79,39 @@ int check_recurrence(const float* q, const float* k, const float* v, const float
   return GDN_OK;
 }
 
+// The norm operands of gdn_layer_chunked (after check_recurrence has passed): z and w are
+// read, y is written; y must overlap nothing else, and the recurrence's writes (o, the
+// state, the workspace) must not overlap z or w.
+int check_layer_norm(const float* q, const float* k, const float* v, const float* g,
+                     const float* beta, const float* state_in, const float* state_out,
+                     const float* o, const void* workspace, size_t ws_bytes, const float* z,
+                     const float* w, float eps, const uint16_t* y, int64_t T, int n_k_heads,
+                     int n_v_heads) {
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GDN_ERR_BAD_SHAPE;
+  if (!w || !y || (T > 0 && !z)) return GDN_ERR_NULL_POINTER;
+  const void* ptrs[] = {z, w, y};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+  if (T == 0) return GDN_OK;
+  const size_t f = sizeof(float), dk = gdn::kDim, dv = gdn::kDim;
+  const size_t qk_b = (size_t)T * n_k_heads * dk * f, v_b = (size_t)T * n_v_heads * dv * f;
+  const size_t gb_b = (size_t)T * n_v_heads * f, s_b = (size_t)n_v_heads * dk * dv * f;
+  const Range r_y = range_of(y, (size_t)T * n_v_heads * dv * sizeof(uint16_t));
+  const Range r_z = range_of(z, v_b), r_w = range_of(w, (size_t)n_v_heads * dv * f);
+  const Range others[] = {range_of(q, qk_b),      range_of(k, qk_b),
+                          range_of(v, v_b),       range_of(g, gb_b),
+                          range_of(beta, gb_b),   range_of(state_in, s_b),
+                          range_of(state_out, s_b), range_of(o, v_b),
+                          range_of(workspace, ws_bytes), r_z, r_w};
+  for (const Range& r : others)
+    if (overlap(r_y, r)) return GDN_ERR_ALIASING;
+  const Range writes[] = {range_of(state_out, s_b), range_of(o, v_b),
+                          range_of(workspace, ws_bytes)};
+  for (const Range& r : writes)
+    if (overlap(r, r_z) || overlap(r, r_w)) return GDN_ERR_ALIASING;
+  return GDN_OK;
+}
+
 int copy_state_if_needed(const float* state_in, float* state_out, int n_v_heads, int dk,
                          int dv, hipStream_t s) {
   if (state_out == state_in) return GDN_OK;
@@ -115,14 +148,28 @@ size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv)
 
 namespace {
 
+// The norm half of gdn_layer_chunked (NULL y: the recurrence alone).
+struct NormOut {
+  const float* z;
+  const float* w;
+  float eps;
+  uint16_t* y;
+};
+
 int chunked_impl(const float* q, const float* k, const float* v, const float* g,
                  const float* beta, const float* state_in, float* state_out, float* o,
                  int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* workspace,
-                 size_t workspace_bytes, void* const* scan_events, int n_scan_events,
-                 void* stream) {
+                 size_t workspace_bytes, const NormOut& nrm, void* const* scan_events,
+                 int n_scan_events, void* stream) {
   if (int st = check_recurrence(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads,
                                 n_v_heads, dk, dv, workspace, workspace_bytes, true))
     return st;
+  if (nrm.y || nrm.z || nrm.w) {
+    if (int st = check_layer_norm(q, k, v, g, beta, state_in, state_out, o, workspace,
+                                  workspace_bytes, nrm.z, nrm.w, nrm.eps, nrm.y, T, n_k_heads,
+                                  n_v_heads))
+      return st;
+  }
   if (n_scan_events > 0 && !scan_events) return GDN_ERR_NULL_POINTER;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) return copy_state_if_needed(state_in, state_out, n_v_heads, dk, dv, s);
@@ -137,21 +184,36 @@ int chunked_impl(const float* q, const float* k, const float* v, const float* g,
                           static_cast<float*>(workspace) + (sb & 1) * half_floats, (int)t0, n,
                           n_k_heads, n_v_heads};
   };
+  // The norm of super-block sb - 1 runs inside launch sb (its o is complete by then); the
+  // last super-block's norm is a launch of its own.
+  auto norm_rows = [&](int sb) {
+    const int64_t t0 = (int64_t)sb * gdn::kSuperBlock;
+    const int n = (int)((T - t0) < gdn::kSuperBlock ? (T - t0) : gdn::kSuperBlock);
+    const size_t off = (size_t)t0 * n_v_heads * dv;
+    return gdn::NormArgs{o + off, nrm.z + off, nrm.w, nrm.y + off, nrm.eps, n * n_v_heads,
+                         n_v_heads};
+  };
   const gdn::ChunkArgs first = sb_args(0);
   hipError_t e = gdn::launch_chunk_prep(first, s);
   if (e != hipSuccess) return hip_fail(e);
   for (int sb = 0; sb < nsb; ++sb) {
     const gdn::ChunkArgs a = sb_args(sb);
     const gdn::ChunkArgs next = sb + 1 < nsb ? sb_args(sb + 1) : a;
+    const gdn::NormArgs prev = nrm.y && sb > 0 ? norm_rows(sb - 1) : gdn::NormArgs{};
     const bool timed = 2 * sb + 1 < n_scan_events;
     if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(scan_events[2 * sb]), s)) !=
                      hipSuccess)
       return hip_fail(e);
-    e = gdn::launch_chunk_scan_fused(a, sb + 1 < nsb ? &next : nullptr, s);
+    e = gdn::launch_chunk_scan_fused(a, sb + 1 < nsb ? &next : nullptr,
+                                     nrm.y && sb > 0 ? &prev : nullptr, s);
     if (e != hipSuccess) return hip_fail(e);
     if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(scan_events[2 * sb + 1]), s)) !=
                      hipSuccess)
       return hip_fail(e);
+  }
+  if (nrm.y) {
+    const gdn::NormArgs last = norm_rows(nsb - 1);
+    if ((e = gdn::launch_out_norm(last, s)) != hipSuccess) return hip_fail(e);
   }
   return GDN_OK;
 }
@@ -165,7 +227,7 @@ int gdn_recurrence_chunked(const float* q, const float* k, const float* v, const
                            float* o, int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
-                      dv, workspace, workspace_bytes, nullptr, 0, stream);
+                      dv, workspace, workspace_bytes, NormOut{}, nullptr, 0, stream);
 }
 
 int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
@@ -175,7 +237,31 @@ int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
                                  size_t workspace_bytes, void* const* scan_events,
                                  int n_scan_events, void* stream) {
   return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
-                      dv, workspace, workspace_bytes, scan_events, n_scan_events, stream);
+                      dv, workspace, workspace_bytes, NormOut{}, scan_events, n_scan_events,
+                      stream);
+}
+
+int gdn_layer_chunked(const float* q, const float* k, const float* v, const float* g,
+                      const float* beta, const float* state_in, float* state_out, float* o,
+                      const float* z, const float* w, float eps, uint16_t* y, int64_t T,
+                      int n_k_heads, int n_v_heads, int dk, int dv, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!y || !w || (T > 0 && !z)) return GDN_ERR_NULL_POINTER;
+  return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
+                      dv, workspace, workspace_bytes, NormOut{z, w, eps, y}, nullptr, 0,
+                      stream);
+}
+
+int gdn_layer_chunked_timed(const float* q, const float* k, const float* v, const float* g,
+                            const float* beta, const float* state_in, float* state_out,
+                            float* o, const float* z, const float* w, float eps, uint16_t* y,
+                            int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                            void* workspace, size_t workspace_bytes,
+                            void* const* scan_events, int n_scan_events, void* stream) {
+  if (!y || !w || (T > 0 && !z)) return GDN_ERR_NULL_POINTER;
+  return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
+                      dv, workspace, workspace_bytes, NormOut{z, w, eps, y}, scan_events,
+                      n_scan_events, stream);
 }
 
 int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint16_t* y,

@@ -516,9 +516,58 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(ChunkArgs a) {
 struct FusedArgs {
   ChunkArgs scan;
   ChunkArgs prep;
+  NormArgs norm;
   int n_scan;  // scan workgroups
   int has_prep;
+  int has_norm;
 };
+
+// The output norm of the previous super-block, run by the three waves of each scan
+// workgroup that the scan leaves free (their vector instructions do not slow the compute
+// waves' matrix products on the same SIMD).  They take part in exactly the scan's barriers
+// (one before the first chunk, one per chunk, nch in all), doing a slice of rows between
+// barriers: half-wave `worker` of `nworkers` owns rows worker + j * nworkers, j = 0 .. 127
+// (n_scan * 6 * 128 >= 2048 * n_v_heads rows), and handles j = c and j = c + 64 between
+// the barriers of chunks c - 1 and c, with the loads of the next slice issued before the
+// arithmetic of this one.  Slices left over (nch < 64) follow the last barrier.
+__device__ __forceinline__ void norm_role(const NormArgs& n, int worker, int nworkers, int nch) {
+  const int p = threadIdx.x & 31;
+  const uint32_t bytes = (uint32_t)n.n_rows * kDim * 4;
+  const buf_rsrc ro = make_rsrc(n.o, bytes), rz = make_rsrc(n.z, bytes);
+  const buf_rsrc ry = make_rsrc(n.y, bytes / 2);
+  f32x4 ov[2][2], zv[2][2];  // [buffer][row of the slice]
+  auto row_of = [&](int j) { return worker + j * nworkers; };
+  auto load = [&](int buf, int c) {  // rows past the end read as 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = ((uint32_t)row_of(c + kChunksPerSB * i) * kDim + 4 * p) * 4;
+      ov[buf][i] = buf_load4(ro, off);
+      zv[buf][i] = buf_load4(rz, off);
+    }
+  };
+  auto finish = [&](int buf, int c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = row_of(c + kChunksPerSB * i);
+      if (r < n.n_rows) {  // whole half-waves: the two halves of a wave may differ
+        const float4 wv =
+            *reinterpret_cast<const float4*>(n.w + (r % n.n_v_heads) * kDim + 4 * p);
+        buf_store2(ry, ((uint32_t)r * kDim + 4 * p) * 2,
+                   gated_rms_row(ov[buf][i], zv[buf][i], wv, n.eps));
+      }
+    }
+  };
+  load(0, 0);
+  barrier_only();
+  for (int c = 0; c < kChunksPerSB; c += 2) {
+    load(1, c + 1);
+    finish(0, c);
+    if (c < nch) barrier_only();
+    if (c + 2 < kChunksPerSB) load(0, c + 2);
+    finish(1, c + 1);
+    if (c + 1 < nch) barrier_only();
+  }
+}
 
 union FusedSmem {
   ScanSmem scan;
@@ -536,7 +585,13 @@ __global__ __launch_bounds__(FUSED_NT) void chunk_fused_kernel(FusedArgs f) {
   __shared__ FusedSmem sm;
   const int b = blockIdx.x;
   if (b < f.n_scan) {
-    if (threadIdx.x < SC_NT) scan_block(f.scan, b, f.n_scan, sm.scan);
+    if (threadIdx.x < SC_NT) {
+      scan_block(f.scan, b, f.n_scan, sm.scan);
+    } else if (f.has_norm) {
+      const int per_wg = (FUSED_NT - SC_NT) / 32;  // norm half-waves per scan workgroup
+      norm_role(f.norm, b * per_wg + (threadIdx.x - SC_NT) / 32, f.n_scan * per_wg,
+                (f.scan.n_tok + kChunk - 1) / kChunk);
+    }
   } else if (f.has_prep) {
     const int Hk = f.prep.n_k_heads;
     const int items = ((f.prep.n_tok + kChunk - 1) / kChunk) * Hk;
@@ -557,10 +612,12 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_next,
-                                   hipStream_t stream) {
+                                   const NormArgs* norm_prev, hipStream_t stream) {
   FusedArgs f;
   f.scan = scan;
   f.prep = prep_next ? *prep_next : scan;
+  f.norm = norm_prev ? *norm_prev : NormArgs{};
+  f.has_norm = norm_prev != nullptr;
   f.n_scan = scan.n_v_heads * (kDim / SC_COLS);
   f.has_prep = prep_next != nullptr;
   // the prep workgroups fill the CUs the scan leaves free (at least 32 of them)

@@ -40,6 +40,35 @@ __device__ __forceinline__ float half_wave_sum(float x) {
                                                                    SWIZZLE_XOR16));
 }
 
+// Gated RMS norm of one (token, value head) row of 128 values held by a half-wave, 4 per
+// lane (lane p of the half holds columns 4p .. 4p+3 of o, z and the head's weight w):
+//     y_j = fp16_rne( o_j * rsqrt(mean(o^2) + eps) * w_j * sigmoid(z_j) )
+// returned as two packed pairs of binary16 bit patterns.  Every kernel that writes y uses
+// this one function, so they agree bit for bit.  The reciprocal square root, 2^x and the
+// reciprocal are the hardware's single instructions (each within about 1 FP32 ulp), far
+// below half an FP16 ulp; the result is then rounded to FP16 by round-to-nearest-even.
+// Must be executed by all 32 lanes of the half.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_half2_rne(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ float sigmoid_hw(float x) {
+  // 1 / (1 + e^{-x}) with e^{-x} = 2^{-x log2(e)}
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+__device__ __forceinline__ u32x2 gated_rms_row(const f32x4 ov, const f32x4 zv, const float4 wv,
+                                               float eps) {
+  float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
+  ss = half_wave_sum(ss);
+  const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / 128) + eps);
+  u32x2 out;
+  out.x = pack_half2_rne(ov.x * rs * wv.x * sigmoid_hw(zv.x), ov.y * rs * wv.y * sigmoid_hw(zv.y));
+  out.y = pack_half2_rne(ov.z * rs * wv.z * sigmoid_hw(zv.z), ov.w * rs * wv.w * sigmoid_hw(zv.w));
+  return out;
+}
+
 // D = A * B + C on a 16x16 tile with a K-step of 4 (v_mfma_f32_16x16x4_f32).
 // Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; the accumulator holds
 // C[4 * (l / 16) + r][l % 16] in register r.
@@ -67,6 +96,9 @@ __device__ __forceinline__ f32x4 buf_load4(buf_rsrc r, uint32_t byte_off) {
 }
 __device__ __forceinline__ void buf_store(buf_rsrc r, uint32_t byte_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store2(buf_rsrc r, uint32_t byte_off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
 }
 
 // Direct global -> LDS load (gfx950): lane l's 16 bytes at byte_off (from the descriptor's

@@ -66,9 +66,11 @@ struct NormArgs {
 hipError_t launch_seq(const SeqArgs& a, int group, hipStream_t stream);
 hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
 // Scan of super-block `scan`; if prep_next is not NULL the same launch also forms the
-// operators of the next super-block (into prep_next->ws, the other workspace half).
+// operators of the next super-block (into prep_next->ws, the other workspace half); if
+// norm_prev is not NULL it also runs the output norm of norm_prev->n_rows rows (those of
+// the previous super-block, whose o was written by the previous launch).
 hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_next,
-                                   hipStream_t stream);
+                                   const NormArgs* norm_prev, hipStream_t stream);
 hipError_t launch_out_norm(const NormArgs& a, hipStream_t stream);
 
 }  // namespace gdn

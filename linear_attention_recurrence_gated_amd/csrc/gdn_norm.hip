@@ -19,27 +19,12 @@ namespace {
 
 constexpr int NT = 256;
 
-__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ void norm_row(const NormArgs& a, int row, int p, const f32x4 ov,
                                          const f32x4 zv) {
   const int h = row % a.n_v_heads;
   const float4 wv = *reinterpret_cast<const float4*>(a.w + h * kDim + 4 * p);
-  float ss = ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w;
-  ss = half_wave_sum(ss);
-  const float rs = 1.0f / sqrtf(ss * (1.0f / kDim) + a.eps);
-  u32x2 out;
-  out.x = pack_half2(ov.x * rs * wv.x * sigmoid(zv.x), ov.y * rs * wv.y * sigmoid(zv.y));
-  out.y = pack_half2(ov.z * rs * wv.z * sigmoid(zv.z), ov.w * rs * wv.w * sigmoid(zv.w));
-  __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(a.y + row * kDim + 4 * p));
+  __builtin_nontemporal_store(gated_rms_row(ov, zv, wv, a.eps),
+                              reinterpret_cast<u32x2*>(a.y + row * kDim + 4 * p));
 }
 
 constexpr int ROWS = 4;  // rows per half-wave per iteration, all loaded before any math

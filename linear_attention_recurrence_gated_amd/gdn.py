@@ -28,6 +28,10 @@ SIGNATURES = {
     "gdn_recurrence_chunked_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
                                           _P, _SZ, _P, _I, _P]),
     "gdn_out_norm": (_I, [_P, _P, _P, _F, _P, _I64, _I, _I, _P]),
+    "gdn_layer_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64, _I, _I,
+                               _I, _I, _P, _SZ, _P]),
+    "gdn_layer_chunked_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64, _I,
+                                     _I, _I, _I, _P, _SZ, _P, _I, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
     "gdn_last_hip_error": (_I, []),
     "gdn_abi_version": (_I, []),
@@ -152,6 +156,39 @@ def recurrence_chunked(q, k, v, g, beta, state_in, state_out=None, o=None, ws=No
                                                 _stream(stream, q.device))
         _check("gdn_recurrence_chunked_timed", st)
     return o, state_out
+
+
+def layer_chunked(q, k, v, g, beta, state_in, z, w, eps=1e-6, state_out=None, o=None, y=None,
+                  ws=None, stream=None, scan_events=None):
+    """Chunked recurrence + gated RMS norm in one call.  Returns (y, o, state_out);
+    ``scan_events`` selects the profiling entry point (events around each recurrence
+    launch)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in"),
+                 (z, "z"), (w, "w")):
+        _f32(t, n)
+    T, Hk, Hv, dk, dv = _shapes(q, v)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    if o is None:
+        o = torch.empty_like(v)
+    if y is None:
+        y = torch.empty(v.shape, dtype=torch.float16, device=v.device)
+    _f32(state_out, "state_out"); _f32(o, "o")
+    if y.dtype != torch.float16 or not y.is_contiguous() or not y.is_cuda:
+        raise TypeError("y must be a contiguous float16 CUDA tensor")
+    if ws is None:
+        ws = workspace(q.device, Hk, Hv, dk, dv)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out),
+            _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(y), T, Hk, Hv, dk, dv, _ptr(ws),
+            ws.numel() * ws.element_size())
+    if scan_events is None:
+        st = lib().gdn_layer_chunked(*args, _stream(stream, q.device))
+        _check("gdn_layer_chunked", st)
+    else:
+        arr = (ctypes.c_void_p * max(1, len(scan_events)))(*scan_events)
+        st = lib().gdn_layer_chunked_timed(*args, arr, len(scan_events), _stream(stream, q.device))
+        _check("gdn_layer_chunked_timed", st)
+    return y, o, state_out
 
 
 def out_norm(o, z, w, eps=1e-6, y=None, stream=None):

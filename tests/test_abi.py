@@ -65,7 +65,8 @@ def _addrs(T=64, Hk=16, Hv=48):
     a = {}
     cur = BASE
     for name, size in (("q", qk), ("k", qk), ("v", vv), ("g", gb), ("beta", gb),
-                       ("s_in", st), ("s_out", st), ("o", vv), ("ws", 2 * 64 * Hv * 2176 * 4)):
+                       ("s_in", st), ("s_out", st), ("o", vv), ("ws", 2 * 64 * Hv * 2176 * 4),
+                       ("z", vv), ("w", Hv * 128 * 4), ("y", vv // 2)):
         a[name] = cur
         cur += (size + MB) & ~(MB - 1)
     return a
@@ -86,7 +87,16 @@ def _chunked(L, a, T=64, Hk=16, Hv=48, ws_bytes=None):
                                     P(a["ws"]), ws_bytes, None)
 
 
-@pytest.mark.parametrize("fn", [_seq, _chunked])
+def _layer(L, a, T=64, Hk=16, Hv=48, ws_bytes=None, eps=1e-6):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = L.gdn_chunked_workspace_bytes(Hk, Hv, 128, 128)
+    return L.gdn_layer_chunked(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                               P(a["s_in"]), P(a["s_out"]), P(a["o"]), P(a["z"]), P(a["w"]), eps,
+                               P(a["y"]), T, Hk, Hv, 128, 128, P(a["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", [_seq, _chunked, _layer])
 def test_recurrence_validation(L, fn):
     a = _addrs()
     assert fn(L, dict(a, q=0)) == NULLP
@@ -132,3 +142,23 @@ def test_out_norm_validation(L):
     assert f(P(o), P(z), P(w), 1e-6, P(y + 2), T, Hv, 128, None) == MISAL
     assert f(P(o), P(z), P(w), 1e-6, P(o + 256), T, Hv, 128, None) == ALIAS
     assert f(P(o), P(z), P(w), 1e-6, P(y), 0, Hv, 128, None) == OK   # nothing to do
+
+
+def test_layer_validation(L):
+    """The norm operands of the one-call layer: the recurrence checks above, plus these."""
+    a = _addrs()
+    assert _layer(L, dict(a, ws=0)) == WS
+    assert _layer(L, a, eps=-1.0) == SHAPE
+    assert _layer(L, a, eps=float("inf")) == SHAPE
+    assert _layer(L, dict(a, y=0)) == NULLP
+    assert _layer(L, dict(a, z=0)) == NULLP
+    assert _layer(L, dict(a, w=0)) == NULLP
+    assert _layer(L, dict(a, y=a["y"] + 2)) == MISAL
+    assert _layer(L, dict(a, z=a["z"] + 4)) == MISAL
+    assert _layer(L, dict(a, y=a["o"] + 256)) == ALIAS      # y over the recurrence output
+    assert _layer(L, dict(a, y=a["q"])) == ALIAS
+    assert _layer(L, dict(a, y=a["ws"])) == ALIAS
+    assert _layer(L, dict(a, y=a["z"])) == ALIAS
+    assert _layer(L, dict(a, o=a["z"])) == ALIAS            # the recurrence writes over z
+    assert _layer(L, dict(a, s_out=a["w"])) == ALIAS        # ... or over w
+    assert _layer(L, dict(a, s_out=a["s_in"]), T=0) == OK   # nothing to do

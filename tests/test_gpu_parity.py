@@ -212,3 +212,53 @@ def test_36_layer_stack():
         bad, worst = y_end_to_end_violations(y_h, o_ref, x["z"][:, heads], x["w"][heads][None],
                                              1e-6, CHUNKED_TOL, y_ref)
         assert bad == 0, worst
+
+
+@pytest.mark.parametrize("T", [1, 100, 2048, 2049, 4099, 6200])
+def test_layer_matches_separate_calls(T):
+    """gdn_layer_chunked (the norm of each super-block run inside the next recurrence
+    launch, the last one on its own) gives the same bits as gdn_recurrence_chunked followed
+    by gdn_out_norm: o, the final state and y; outputs are NaN-filled beforehand."""
+    from linear_attention_recurrence_gated_amd import gdn
+    x = make_inputs(T, seed=5, with_norm=True)
+    d = to_dev(x)
+    log("layer vs separate T=%d" % T)
+    o1, s1 = gdn.recurrence_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    y1 = gdn.out_norm(o1, d["z"], d["w"], eps=1e-6)
+    y2, o2, s2 = gdn.layer_chunked(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"], d["w"], eps=1e-6,
+        state_out=_nan_like(d["s0"]), o=_nan_like(d["v"]),
+        y=torch.full(d["v"].shape, float("nan"), dtype=torch.float16, device=d["v"].device))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_layer_t32768_against_oracle():
+    """One layer in one call at T = 32768: o and the state of six heads against the oracle
+    (recurrence gate), y of the same heads within the end-to-end bound; a second call gives
+    the same bits."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    x = make_inputs(32768, seed=3, with_norm=True)
+    d = to_dev(x)
+    heads = [1, 17, 33, 6, 22, 47]
+    log("layer T=32768")
+    y, o, s = gdn.layer_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"],
+                                d["w"], eps=1e-6)
+    torch.cuda.synchronize()
+    y_h, o_h, s_h = y.cpu().numpy(), o.cpu().numpy(), s.cpu().numpy()
+    o_ref, s_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"],
+                                     heads=heads)
+    eo, es = rel_err(o_h[:, heads], o_ref), rel_err(s_h[heads], s_ref)
+    log("  out %.3e state %.3e" % (eo, es))
+    assert eo <= CHUNKED_TOL and es <= CHUNKED_TOL
+    y_ref = oracle.out_norm(o_ref, x["z"][:, heads], x["w"], 1e-6, heads=heads)
+    bad, worst = y_end_to_end_violations(y_h[:, heads], o_ref, x["z"][:, heads],
+                                         x["w"][heads][None], 1e-6, CHUNKED_TOL, y_ref)
+    assert bad == 0, worst
+    y2, _, _ = gdn.layer_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"],
+                                 d["w"], eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
