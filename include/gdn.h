@@ -146,6 +146,21 @@ int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint
                  int64_t T, int n_v_heads, int dv, void* stream);
 
 /*
+ * The recurrence with the kernel chosen by T: gdn_recurrence_seq for T < GDN_CHUNKED_MIN_T,
+ * gdn_recurrence_chunked otherwise (same arguments and results as the call it picks).
+ * ("#1372 DeltaNet recurrence: STRATA_GDN_CHUNKED=1", sections "What it does" and
+ * "Measured": the chunked path loses to the sequential kernel for short prompts, and the
+ * pages set a minimum length for it on their card.  On an MI355X the two cross at about
+ * 32 tokens, one chunk: 16 tokens take 29 vs 33 us, 32 tokens 36 vs 34 us, 64 tokens 49
+ * vs 36 us, including the launch.)  The workspace may be NULL when T < GDN_CHUNKED_MIN_T.
+ */
+#define GDN_CHUNKED_MIN_T 32
+int gdn_recurrence(const float* q, const float* k, const float* v, const float* g,
+                   const float* beta, const float* state_in, float* state_out, float* o,
+                   int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * One layer's prompt path: the chunked recurrence (gdn_recurrence_chunked, same
  * arguments, same results bit for bit) followed by the gated RMS output norm
  * (gdn_out_norm with z, w, eps, y, same results bit for bit), in one call.  The norm of

@@ -241,6 +241,17 @@ int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
                       stream);
 }
 
+int gdn_recurrence(const float* q, const float* k, const float* v, const float* g,
+                   const float* beta, const float* state_in, float* state_out, float* o,
+                   int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (T < GDN_CHUNKED_MIN_T)
+    return gdn_recurrence_seq(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads,
+                              n_v_heads, dk, dv, stream);
+  return gdn_recurrence_chunked(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads,
+                                n_v_heads, dk, dv, workspace, workspace_bytes, stream);
+}
+
 int gdn_layer_chunked(const float* q, const float* k, const float* v, const float* g,
                       const float* beta, const float* state_in, float* state_out, float* o,
                       const float* z, const float* w, float eps, uint16_t* y, int64_t T,

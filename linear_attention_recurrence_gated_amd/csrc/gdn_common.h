@@ -28,8 +28,10 @@ constexpr int SWIZZLE_XOR16 = 0x401F;   // ds_swizzle bit mode: and 0x1f, or 0, 
 
 // Sum over the 32 lanes of each half of the wave; every lane receives its half's sum.
 // Four DPP steps reduce inside a row of 16 lanes; ds_swizzle (lane ^ 16 within each 32)
-// then adds the other row of the half.  (v_permlane16_swap would do this last step on the
-// VALU, but this compiler returns the same register for both results of its builtin.)
+// then adds the other row of the half.  (v_permlane16_swap does this last step on the VALU;
+// this compiler's builtin for it uses the first result in place of the second, and written
+// as inline assembly with its wait states it made the sequential kernel 14 % slower, which
+// issues six of these reductions per token and overlaps the swizzles' latencies.)
 // Must be executed by all 32 lanes of the half.
 __device__ __forceinline__ float half_wave_sum(float x) {
   x += dpp_mov<DPP_XOR1>(x);

@@ -28,6 +28,7 @@ SIGNATURES = {
     "gdn_recurrence_chunked_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
                                           _P, _SZ, _P, _I, _P]),
     "gdn_out_norm": (_I, [_P, _P, _P, _F, _P, _I64, _I, _I, _P]),
+    "gdn_recurrence": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _P, _SZ, _P]),
     "gdn_layer_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64, _I, _I,
                                _I, _I, _P, _SZ, _P]),
     "gdn_layer_chunked_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64, _I,
@@ -155,6 +156,30 @@ def recurrence_chunked(q, k, v, g, beta, state_in, state_out=None, o=None, ws=No
         st = lib().gdn_recurrence_chunked_timed(*args, arr, len(scan_events),
                                                 _stream(stream, q.device))
         _check("gdn_recurrence_chunked_timed", st)
+    return o, state_out
+
+
+CHUNKED_MIN_T = 32  # GDN_CHUNKED_MIN_T of gdn.h
+
+
+def recurrence(q, k, v, g, beta, state_in, state_out=None, o=None, ws=None, stream=None):
+    """The recurrence with the kernel chosen by T (sequential below CHUNKED_MIN_T tokens,
+    chunked from there).  Returns (o, state_out)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in")):
+        _f32(t, n)
+    T, Hk, Hv, dk, dv = _shapes(q, v)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    if o is None:
+        o = torch.empty_like(v)
+    _f32(state_out, "state_out"); _f32(o, "o")
+    if ws is None and T >= CHUNKED_MIN_T:
+        ws = workspace(q.device, Hk, Hv, dk, dv)
+    ws_ptr, ws_bytes = (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+    st = lib().gdn_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                              _ptr(state_out), _ptr(o), T, Hk, Hv, dk, dv, ws_ptr, ws_bytes,
+                              _stream(stream, q.device))
+    _check("gdn_recurrence", st)
     return o, state_out
 
 

@@ -162,3 +162,24 @@ def test_layer_validation(L):
     assert _layer(L, dict(a, o=a["z"])) == ALIAS            # the recurrence writes over z
     assert _layer(L, dict(a, s_out=a["w"])) == ALIAS        # ... or over w
     assert _layer(L, dict(a, s_out=a["s_in"]), T=0) == OK   # nothing to do
+
+
+def _auto(L, a, T=64, Hk=16, Hv=48, ws_bytes=None):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = L.gdn_chunked_workspace_bytes(Hk, Hv, 128, 128)
+    return L.gdn_recurrence(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                            P(a["s_in"]), P(a["s_out"]), P(a["o"]), T, Hk, Hv, 128, 128,
+                            P(a["ws"]), ws_bytes, None)
+
+
+def test_auto_dispatch_validation(L):
+    """gdn_recurrence validates as the kernel it picks: from 32 tokens on the chunked path
+    (which needs the workspace), below that the sequential one (which does not)."""
+    a = _addrs()
+    assert _auto(L, dict(a, ws=0), T=64) == WS
+    assert _auto(L, a, T=32, ws_bytes=1024) == WS
+    assert _auto(L, dict(a, q=0), T=16) == NULLP
+    assert _auto(L, dict(a, o=a["q"]), T=8) == ALIAS
+    assert _auto(L, a, T=16, Hv=40) == SHAPE
+    assert _auto(L, dict(a, ws=0, s_out=a["s_in"]), T=0) == OK   # nothing to do

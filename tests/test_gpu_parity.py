@@ -262,3 +262,40 @@ def test_layer_t32768_against_oracle():
                                  d["w"], eps=1e-6)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [5, 31, 32, 100])
+def test_auto_dispatch(T):
+    """gdn_recurrence gives the sequential kernel's bits below 32 tokens and the chunked
+    path's from 32 on."""
+    from linear_attention_recurrence_gated_amd import gdn
+    x = make_inputs(T, seed=9)
+    d = to_dev(x)
+    o, s = gdn.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    kind = "seq" if T < gdn.CHUNKED_MIN_T else "chunked"
+    o_ref, s_ref = run(kind, d)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int32), o_ref.view(torch.int32))
+    assert torch.equal(s.view(torch.int32), s_ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("hk,hv", [(4, 4), (8, 16), (2, 8)])
+def test_layer_other_group_sizes(hk, hv):
+    """The one-call layer with 1, 2 and 4 value heads per key head over three super-blocks
+    (the norm of each earlier super-block spread over that head count's scan workgroups):
+    the same bits as the two separate calls."""
+    from linear_attention_recurrence_gated_amd import gdn
+    T = 4200
+    x = make_inputs(T, seed=hv + 1, n_k_heads=hk, n_v_heads=hv, with_norm=True)
+    d = to_dev(x)
+    log("layer Hk=%d Hv=%d" % (hk, hv))
+    ws = gdn.workspace(d["q"].device, hk, hv)
+    o1, s1 = gdn.recurrence_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], ws=ws)
+    y1 = gdn.out_norm(o1, d["z"], d["w"], eps=1e-6)
+    torch.cuda.synchronize()
+    y2, o2, s2 = gdn.layer_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"],
+                                   d["w"], eps=1e-6, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
