@@ -206,19 +206,19 @@ constexpr int SC_RING = 3;   // chunk buffers in LDS
 __device__ __forceinline__ int sw8(int i) { return (i ^ (i >> 3)) & 7; }
 __device__ __forceinline__ int swv(int t) { return ((t >> 2) & 1) << 2; }
 
-struct ScanBuf {
-  f32x4 k[kChunk * 32];
-  f32x4 q[kChunk * 32];
-  f32x4 T[kChunk * 8];
-  f32x4 P[kChunk * 8];
-  f32x4 misc[64];
-  f32x4 v[kChunk * SC_COLS / 4];
-};
-
 constexpr int SC_XCHG = 2 * 2 * 2 * 3 * 64;  // [parity][col slice][row half][tile][lane]
 
+// The ring is laid out array by array (the K tiles of all ring positions, then the Q
+// tiles, ...), so that each of a lane's read patterns reaches its tile in every ring
+// position from one base register plus an immediate offset below 64 KiB (the reach of an
+// LDS instruction's offset field): no address arithmetic inside the chunk loop.
 struct ScanSmem {
-  ScanBuf buf[SC_RING];
+  f32x4 k[SC_RING][kChunk * 32];
+  f32x4 q[SC_RING][kChunk * 32];
+  f32x4 T[SC_RING][kChunk * 8];
+  f32x4 P[SC_RING][kChunk * 8];
+  f32x4 misc[SC_RING][64];
+  f32x4 v[SC_RING][kChunk * SC_COLS / 4];
   f32x4 x[SC_XCHG];
 };
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "LDS of one CU");
@@ -271,83 +271,115 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
   const int t00_i = lc * 8 + (q4 ^ sw8(lc));
   const int t10_i = (16 + lc) * 8 + (q4 ^ sw8(16 + lc));
   const int t11_i = (16 + lc) * 8 + ((4 + q4) ^ sw8(16 + lc));
-  const int pa_i = RH ? t10_i : t00_i;      // P tile (RH, 0)
+  // P tiles of this wave's share of P D: row half 0 takes tile (0,0) and steps 0, 1 of
+  // tile (1,0); row half 1 steps 2, 3 of tile (1,0) and tile (1,1) (six products each).
+  const int pa_i = RH ? t10_i : t00_i;
+  const int pb_i = RH ? t11_i : t10_i;
   // float in v: token lr (+ r, + 16 tt), column colw
   const int vv_i = (lr * 8 + ((colw >> 2) ^ ((q4 & 1) << 2))) * 4 + (colw & 3);
-  const int xw_i = (cs * 2 + RH) * 3 * 64 + l;  // exchange: this wave's tiles
-  const int xr_i = cs * 2 * 3 * 64 + l;         // exchange: row half 0 of the column slice
+  // Exchange area of the column slice, [row half][tile][lane] from here: tiles 0, 1 the
+  // partial K S0 of each token tile, tile 2 the part of the other half's output tile.
+  const f32x4* const xs = sm.x + cs * 2 * 3 * 64 + l;
+  constexpr int XW = 192 * RH, XP = 192 * (1 - RH) + 128;  // this half's tiles, partner's part
 
   // O stores of token 16 RH + lr + r of a chunk
   uint32_t o_off[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) o_off[r] = (((16 * RH + lr + r) * Hv + h) * kDim + col) * 4;
 
-  // Descriptors of chunk c: its tokens onward (an empty range past the end, so loads
-  // return 0 and stores are dropped) and its workspace slot (clamped to the last chunk).
-  auto tok_rsrc = [&](const float* base, int row_floats, int c) {
-    return rsrc_range(base + (size_t)(a.t_begin + c * kChunk) * row_floats,
-                      (a.n_tok - c * kChunk) * row_floats * 4);
+
+  // Output tile RH of chunk c - 1: this wave's part plus the other half's, which arrives
+  // with the barrier of chunk c.  For c = 0 the range is empty and the stores are dropped.
+  auto store_prev_o = [&](const f32x4 own, const f32x4 other, int c) {
+    const f32x4 O = own + other;
+    const int cp = c > 0 ? c - 1 : 0;
+    const buf_rsrc ro = rsrc_range(a.o + (size_t)(a.t_begin + cp * kChunk) * Hv * kDim,
+                                   c > 0 ? (a.n_tok - cp * kChunk) * Hv * kDim * 4 : 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buf_store(ro, o_off[r], O[r]);  // dropped past the end
   };
+  f32x4 Oprev = f32x4{0.f, 0.f, 0.f, 0.f};  // this wave's part of the previous output tile
+
   auto step = [&](auto rbc, int c) {
     constexpr int RB = decltype(rbc)::value;
-    const ScanBuf& B = sm.buf[RB];
-    const float* kf = reinterpret_cast<const float*>(B.k);
-    const float* vf = reinterpret_cast<const float*>(B.v);
+    const float* kf = reinterpret_cast<const float*>(sm.k[RB]);
+    const float* vf = reinterpret_cast<const float*>(sm.v[RB]);
 
-    // (a) This chunk's operands (loaded and published before the previous barrier).
+    // (a) This chunk's operands (published by the previous barrier; the buffer is reloaded
+    //     after this chunk's barrier, so everything is read before it).
     f32x4 ka[4][2], qa[4][2];
     float kt[4][2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        ka[rt][tt] = B.k[ka_i[rt] + 16 * 32 * tt];
-        qa[rt][tt] = B.q[ka_i[rt] + 16 * 32 * tt];
+        ka[rt][tt] = sm.k[RB][ka_i[rt] + 16 * 32 * tt];
+        qa[rt][tt] = sm.q[RB][ka_i[rt] + 16 * 32 * tt];
 #pragma unroll
         for (int r = 0; r < 4; ++r) kt[rt][tt][r] = kf[kt_i[rt][r] + 16 * 32 * 4 * tt];
       }
-    const f32x4 T00 = B.T[t00_i], T10 = B.T[t10_i], T11 = B.T[t11_i];
-    const f32x4 Pa = B.P[pa_i], Pb = B.P[t11_i];
+    const f32x4 T00 = sm.T[RB][t00_i], T10 = sm.T[RB][t10_i], T11 = sm.T[RB][t11_i];
+    const f32x4 Pa = sm.P[RB][pa_i], Pb = sm.P[RB][pb_i];
     f32x4 eg[2], eb[2], vv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      eg[tt] = B.misc[4 * tt + q4];
-      eb[tt] = B.misc[8 + 4 * tt + q4];
+      eg[tt] = sm.misc[RB][4 * tt + q4];
+      eb[tt] = sm.misc[RB][8 + 4 * tt + q4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) vv[tt][r] = vf[vv_i + 32 * r + 16 * 32 * tt];
     }
-    const float egl = reinterpret_cast<const float*>(B.misc)[64];
+    const float egl = reinterpret_cast<const float*>(sm.misc[RB])[64];
 
-    // (b) Partial K S0 and Q S0 over this wave's 64 rows; the state registers are the B
-    //     operand as they are.
-    f32x4 P4[4];  // partial W0, W1, QS0, QS1
+    // (b) Partial K S0 over this wave's 64 rows (the state registers are the B operand as
+    //     they are), then partial Q S0, whose products cover the exchange: a few before
+    //     the partial K S0 is written, the rest after the barrier while it is read back.
+    f32x4 Wp[2], Qp[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) P4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) Wp[i] = Qp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          P4[tt] = mfma16x16x4(ka[rt][tt][r], S[rt][r], P4[tt]);
-          P4[2 + tt] = mfma16x16x4(qa[rt][tt][r], S[rt][r], P4[2 + tt]);
-        }
+        for (int tt = 0; tt < 2; ++tt) Wp[tt] = mfma16x16x4(ka[rt][tt][r], S[rt][r], Wp[tt]);
+    auto qs = [&](int rt, int r) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) Qp[tt] = mfma16x16x4(qa[rt][tt][r], S[rt][r], Qp[tt]);
+    };
+    qs(0, 0);
+    qs(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // (c) Exchange with the other row half of the same columns: both W partials and the
-    //     Q S0 partial of the other half's output tile.  (The producer has published
-    //     chunk c + 1 by the same barrier.)
-    const int xo = (c & 1) * (SC_XCHG / 2);
-    sm.x[xo + xw_i] = P4[0];
-    sm.x[xo + xw_i + 64] = P4[1];
-    sm.x[xo + xw_i + 128] = RH ? P4[2] : P4[3];
+    // (c) Exchange with the other row half of the same columns: the two K S0 partials of
+    //     this chunk go out; the other half's part of the previous chunk's output tile
+    //     comes in.  (The producer has published chunk c + 1 by the same barrier.)
+    f32x4* const xc = const_cast<f32x4*>(xs) + (c & 1) * (SC_XCHG / 2);  // this chunk's
+    f32x4* const xn = const_cast<f32x4*>(xs) + (~c & 1) * (SC_XCHG / 2);  // the next one's
+    xc[XW] = Wp[0];
+    xc[XW + 64] = Wp[1];
+    qs(0, 2);
+    qs(0, 3);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vm_lgkm0<63>();  // LDS writes done; the O stores may still be in flight
     barrier_only();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 Wx[2][2];  // [row half][token tile]
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      Wx[0][tt] = xc[64 * tt];
+      Wx[1][tt] = xc[192 + 64 * tt];
+    }
+    const f32x4 Xprev = xc[XP];
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out before the products below
+#pragma unroll
+    for (int rt = 1; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qs(rt, r);
+    store_prev_o(Oprev, Xprev, c);
     // Both halves add the two partials in the same order, so they hold identical sums.
     f32x4 W[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) W[tt] = sm.x[xo + xr_i + 64 * tt] + sm.x[xo + xr_i + 192 + 64 * tt];
-    const f32x4 QSo = sm.x[xo + xr_i + 192 * (1 - RH) + 128];
-    const f32x4 QSf = RH ? (QSo + P4[3]) : (P4[2] + QSo);
+    for (int tt = 0; tt < 2; ++tt) W[tt] = Wx[0][tt] + Wx[1][tt];
 
     // (d) U = V - e^{gamma} (K S0), C layout: token 16 tt + lr + r, column col.
     f32x4 U[2];
@@ -366,17 +398,24 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
 #pragma unroll
     for (int r = 0; r < 4; ++r) D[1] = mfma16x16x4(T11[r], U[1][r], D[1]);
 
-    // (f) Outputs of token tile RH: O = e^{gamma} Q S0 + P D (P lower triangular).
-    f32x4 O = eg[RH] * QSf;
+    // (f) Outputs O = e^{gamma} Q S0 + P D (P lower triangular).  Token tile RH is this
+    //     wave's; its part here covers its own rows of Q S0, the other half's part (sent
+    //     at the next barrier) the rest.
+    f32x4 own = eg[RH] * Qp[RH];
+    f32x4 other = eg[1 - RH] * Qp[1 - RH];
+    if (RH == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) O = mfma16x16x4(Pa[r], D[0][r], O);
-    if (RH == 1) {
+      for (int r = 0; r < 4; ++r) own = mfma16x16x4(Pa[r], D[0][r], own);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) O = mfma16x16x4(Pb[r], D[1][r], O);
+      for (int r = 0; r < 2; ++r) other = mfma16x16x4(Pb[r], D[0][r], other);
+    } else {
+#pragma unroll
+      for (int r = 2; r < 4; ++r) own = mfma16x16x4(Pa[r], D[0][r], own);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) own = mfma16x16x4(Pb[r], D[1][r], own);
     }
-    const buf_rsrc ro = tok_rsrc(a.o, Hv * kDim, c);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) buf_store(ro, o_off[r], O[r]);  // dropped past the end
+    Oprev = own;
+    xn[XW + 128] = other;  // read after the next barrier
 
     // (g) S' = e^{gamma_last} S0 + K^T diag(e^{gamma_last - gamma}) D.
     f32x4 Dh[2];
@@ -390,6 +429,7 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) S[rt] = mfma16x16x4(kt[rt][tt][r], Dh[tt][r], S[rt]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   barrier_only();  // chunk 0 published by the producer
@@ -400,6 +440,10 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     if (c + 2 >= nch) break;
     step(ic<2>(), c + 2);
   }
+  // The last chunk's output tile: one more barrier brings the other half's part.
+  wait_vm_lgkm0<63>();
+  barrier_only();
+  store_prev_o(Oprev, xs[(nch & 1) * (SC_XCHG / 2) + XP], nch);
 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -410,7 +454,8 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
 
 // The producer wave of a scan workgroup: all direct loads of every chunk, and the waits
 // that make a chunk's operands complete before the barrier that publishes them.  It meets
-// the compute waves at the same barriers (one before the first chunk, one per chunk).
+// the compute waves at the same barriers (one before the first chunk, one per chunk, one
+// after the last).
 constexpr int SC_DMA = 45;  // direct loads per chunk: K 16, Q 16, T 4, P 4, decays 1, V 4
 
 __device__ __forceinline__ void scan_producer(const ChunkArgs& a, int h, int kh, int cblk,
@@ -446,18 +491,18 @@ __device__ __forceinline__ void scan_producer(const ChunkArgs& a, int h, int kh,
                      (a.n_tok - c * kChunk) * row_floats * 4);
   };
   auto issue = [&](auto rbc, int c) {
-    constexpr int B0 = offsetof(ScanSmem, buf) + decltype(rbc)::value * (int)sizeof(ScanBuf);
+    constexpr int RB = decltype(rbc)::value;
     const i32x4 dk = tok_desc(a.k, Hk * kDim, c), dq = tok_desc(a.q, Hk * kDim, c);
     const i32x4 dv = tok_desc(a.v, Hv * kDim, c);
     const i32x4 dw = make_desc(a.ws + ((size_t)min(c, nch - 1) * Hv + h) * kSlot, kSlot * 4);
     const auto s16 = std::make_integer_sequence<int, 16>();
     const auto s4 = std::make_integer_sequence<int, 4>();
-    dma16_run<B0 + offsetof(ScanBuf, k)>(dk, off_kq, lds, s16);
-    dma16_run<B0 + offsetof(ScanBuf, q)>(dq, off_kq, lds, s16);
-    dma16_run<B0 + offsetof(ScanBuf, T)>(dw, off_t, lds, s4);
-    dma16_run<B0 + offsetof(ScanBuf, P)>(dw, off_p, lds, s4);
-    dma16_run<B0 + offsetof(ScanBuf, v)>(dv, off_v, lds, s4);
-    dma16<B0 + offsetof(ScanBuf, misc)>(dw, off_m, lds);
+    dma16_run<offsetof(ScanSmem, k) + RB * sizeof(sm.k[0])>(dk, off_kq, lds, s16);
+    dma16_run<offsetof(ScanSmem, q) + RB * sizeof(sm.q[0])>(dq, off_kq, lds, s16);
+    dma16_run<offsetof(ScanSmem, T) + RB * sizeof(sm.T[0])>(dw, off_t, lds, s4);
+    dma16_run<offsetof(ScanSmem, P) + RB * sizeof(sm.P[0])>(dw, off_p, lds, s4);
+    dma16_run<offsetof(ScanSmem, v) + RB * sizeof(sm.v[0])>(dv, off_v, lds, s4);
+    dma16<offsetof(ScanSmem, misc) + RB * sizeof(sm.misc[0])>(dw, off_m, lds);
   };
   // At the barrier of chunk c the loads of chunk c + 1 must have landed; those of chunk
   // c + 2 (issued after the previous barrier) may still be in flight.  After it, every
@@ -480,6 +525,7 @@ __device__ __forceinline__ void scan_producer(const ChunkArgs& a, int h, int kh,
     publish();
     issue(ic<2>(), c + 5);
   }
+  barrier_only();  // the compute waves' last exchange
   // Loads past the last chunk (never read) must land before the workgroup's LDS is
   // released.
   wait_vm_lgkm0<0>();
@@ -525,11 +571,11 @@ struct FusedArgs {
 // The output norm of the previous super-block, run by the three waves of each scan
 // workgroup that the scan leaves free (their vector instructions do not slow the compute
 // waves' matrix products on the same SIMD).  They take part in exactly the scan's barriers
-// (one before the first chunk, one per chunk, nch in all), doing a slice of rows between
+// (one before the first chunk, one per chunk, one after the last), doing a slice of rows between
 // barriers: half-wave `worker` of `nworkers` owns rows worker + j * nworkers, j = 0 .. 127
 // (n_scan * 6 * 128 >= 2048 * n_v_heads rows), and handles j = c and j = c + 64 between
 // the barriers of chunks c - 1 and c, with the loads of the next slice issued before the
-// arithmetic of this one.  Slices left over (nch < 64) follow the last barrier.
+// arithmetic of this one.  Slices left over (nch < 64) run before the final barrier.
 __device__ __forceinline__ void norm_role(const NormArgs& n, int worker, int nworkers, int nch) {
   const int p = threadIdx.x & 31;
   const uint32_t bytes = (uint32_t)n.n_rows * kDim * 4;
@@ -567,6 +613,7 @@ __device__ __forceinline__ void norm_role(const NormArgs& n, int worker, int nwo
     finish(1, c + 1);
     if (c + 1 < nch) barrier_only();
   }
+  barrier_only();  // the compute waves' last exchange
 }
 
 union FusedSmem {
