@@ -445,11 +445,15 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
   barrier_only();
   store_prev_o(Oprev, xs[(nch & 1) * (SC_XCHG / 2) + XP], nch);
 
+  // The state goes out through 32-bit buffer offsets recomputed here from the lane id (not
+  // addresses kept from before the loop, which would occupy registers all along it).
+  const int lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const buf_rsrc rs = make_rsrc(a.s_dst + (size_t)h * kDim * kDim, kDim * kDim * 4);
+  const uint32_t s_off = ((64 * RH + 4 * (lid >> 4)) * kDim + cblk * SC_COLS + 16 * cs + (lid & 15)) * 4;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      a.s_dst[((size_t)h * kDim + 64 * RH + 16 * rt + lr + r) * kDim + col] = S[rt][r];
+    for (int r = 0; r < 4; ++r) buf_store(rs, s_off + (16 * rt + r) * kDim * 4, S[rt][r]);
 }
 
 // The producer wave of a scan workgroup: all direct loads of every chunk, and the waits
