@@ -17,14 +17,17 @@
 //    decay differences keep full FP32 accuracy; T comes from forward substitution with one
 //    lane per column.  It writes T diag(beta), P and the decay vectors of the key head's
 //    value heads into the caller's workspace.
-//  - scan: one workgroup per (value head, 16*CSB value columns), 2*CSB waves.  Each wave
-//    owns 64 key rows x 16 value columns of the state as four MFMA accumulator tiles that
-//    stay in VGPRs for the whole super-block.  K S0 and Q S0 are accumulated over the
-//    wave's 64 rows on the matrix cores (the state registers are the B operand as they
-//    are), the two row halves exchange partial sums through LDS (one barrier per chunk),
-//    then D = T U, O = e^{gamma} Q S0 + P D and the rank-32 state update K^T D run as
-//    further 16x16x4 MFMAs.  K and Q of the next chunk are staged through double-buffered
-//    LDS while the current chunk computes.
+//  - scan: one workgroup per (value head, 32 value columns): four compute waves, each
+//    owning 64 key rows x 16 value columns of the state as four MFMA accumulator tiles that
+//    stay in VGPRs for the whole super-block, a producer wave that copies every chunk's
+//    operands into a three-buffer LDS ring with direct loads, and three waves that run the
+//    output norm of the previous super-block.  Per chunk, K S0 and Q S0 are accumulated
+//    over each wave's 64 rows on the matrix cores (the state registers are the B operand as
+//    they are), the two row halves exchange partial sums through LDS at one barrier, then
+//    D = T U, O = e^{gamma} Q S0 + P D and the rank-32 state update K^T D run as further
+//    16x16x4 MFMAs.
+//  - the prep of super-block n+1 runs on the CUs the scan of n leaves free, in the same
+//    launch.
 #include <cstddef>
 #include <type_traits>
 
