@@ -84,8 +84,10 @@ __device__ __forceinline__ void stage_store(SeqSmem<G>& sm, int buf, const SeqSt
     const int tt = (tid >> 5) + 8 * m;
     *reinterpret_cast<float4*>(&sm.k[buf][tt][4 * p]) = st.k[m];
     *reinterpret_cast<float4*>(&sm.q[buf][tt][4 * p]) = st.q[m];
-    part[m] = st.k[m].x * st.q[m].x + st.k[m].y * st.q[m].y + st.k[m].z * st.q[m].z +
-              st.k[m].w * st.q[m].w;
+    // explicit fused operations: the prologue's copy of this code and the loop's must
+    // evaluate k.q alike (left to the compiler, they may be contracted differently)
+    part[m] = fmaf(st.k[m].w, st.q[m].w,
+                   fmaf(st.k[m].z, st.q[m].z, fmaf(st.k[m].y, st.q[m].y, st.k[m].x * st.q[m].x)));
   }
   // each half-wave holds one token's k and q rows
 #pragma unroll

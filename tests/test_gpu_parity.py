@@ -119,6 +119,28 @@ def test_in_place_state_and_split(kind):
     assert rel_err(st.cpu().numpy(), s_ref) <= TOL[kind]
 
 
+
+@pytest.mark.parametrize("kind,T,T1", [("seq", 3413, 1000), ("seq", 3413, 2048),
+                                       ("chunked", 5461, 2048), ("chunked", 5461, 4096)])
+def test_split_calls_bitwise(kind, T, T1):
+    """Two calls chained through the state give the bits of one call over the same tokens:
+    anywhere for the sequential kernel (every token runs the same arithmetic, whichever
+    tile of a call it falls in, the first included), at a super-block boundary for the
+    chunked path (elsewhere the chunk partition, hence the rounding, changes)."""
+    x = make_inputs(T, seed=13)
+    d = to_dev(x)
+    o, s = run(kind, d)
+    parts = []
+    st = d["s0"]
+    for a, b in ((0, T1), (T1, T)):
+        dd = {n: d[n][a:b].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        dd["s0"] = st
+        oo, st = run(kind, dd)
+        parts.append(oo)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int32), torch.cat(parts).view(torch.int32))
+    assert torch.equal(s.view(torch.int32), st.view(torch.int32))
+
 @pytest.mark.parametrize("kind", ["seq", "chunked"])
 def test_zero_tokens_copies_state(kind):
     x = make_inputs(4, seed=1)
@@ -299,3 +321,80 @@ def test_layer_other_group_sizes(hk, hv):
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_maximum_token_count():
+    """The largest T the entry points accept for 16 key / 48 value heads (T * 48 * 128 <
+    2^31: 349525 tokens, 171 super-blocks, the last one 1365 tokens), inputs drawn on the
+    device from a seeded generator with the distributions of the parity workloads.  For
+    both recurrence kernels: a call split at the last super-block boundary, the state
+    carried, gives the full call's bits; the last 1365 tokens and the final state match the
+    oracle run from the state at the split.  The one-call layer gives the chunked call's o
+    and state bits, and its y is within one ulp of the oracle's norm of that o on the first,
+    a middle and the last super-block."""
+    import math
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    Hk, Hv, D = 16, 48, 128
+    T = ((1 << 31) - 1) // (Hv * D)
+    T1 = (T // 2048) * 2048
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+
+    def unit(shape):
+        x = torch.randn(shape, device=dev, generator=gen)
+        return x / x.norm(dim=-1, keepdim=True)
+
+    log("maximum T=%d (split at %d): drawing inputs" % (T, T1))
+    q = unit((T, Hk, D)) / math.sqrt(D)
+    k = unit((T, Hk, D))
+    v = torch.randn((T, Hv, D), device=dev, generator=gen)
+    g = -torch.exp(torch.rand((T, Hv), device=dev, generator=gen) * 4.0 - 4.0)
+    beta = torch.sigmoid(torch.randn((T, Hv), device=dev, generator=gen))
+    s0 = 0.1 * torch.randn((Hv, D, D), device=dev, generator=gen)
+    ws = gdn.workspace(dev, Hk, Hv)
+    tail = {n: t[T1:].cpu().numpy() for n, t in (("q", q), ("k", k), ("v", v), ("g", g),
+                                                  ("beta", beta))}
+
+    def call(kind, a, b, s_in):
+        args = (q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], s_in)
+        if kind == "seq":
+            return gdn.recurrence_seq(*args)
+        return gdn.recurrence_chunked(*args, ws=ws)
+
+    o_chunked = s_chunked = None
+    for kind in ("chunked", "seq"):
+        log("  %s: full call" % kind)
+        o, s = call(kind, 0, T, s0)
+        log("  %s: split call" % kind)
+        o1, s1 = call(kind, 0, T1, s0)
+        o2, s2 = call(kind, T1, T, s1)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:T1].view(torch.int32), o1.view(torch.int32))
+        assert torch.equal(o[T1:].view(torch.int32), o2.view(torch.int32))
+        assert torch.equal(s.view(torch.int32), s2.view(torch.int32))
+        o_ref, s_ref = oracle.recurrence(tail["q"], tail["k"], tail["v"], tail["g"],
+                                         tail["beta"], s1.cpu().numpy())
+        eo, es = rel_err(o2.cpu().numpy(), o_ref), rel_err(s2.cpu().numpy(), s_ref)
+        log("  %s: last %d tokens out %.3e state %.3e" % (kind, T - T1, eo, es))
+        assert eo <= TOL[kind] and es <= TOL[kind]
+        if kind == "chunked":
+            o_chunked, s_chunked = o, s
+        del o1, o2, s1, s2
+        if kind == "seq":
+            del o, s
+
+    log("  layer")
+    z = torch.randn((T, Hv, D), device=dev, generator=gen)
+    w = 1.0 + 0.1 * torch.randn((Hv, D), device=dev, generator=gen)
+    y, o, s = gdn.layer_chunked(q, k, v, g, beta, s0, z, w, eps=1e-6, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int32), o_chunked.view(torch.int32))
+    assert torch.equal(s.view(torch.int32), s_chunked.view(torch.int32))
+    w_h = w.cpu().numpy()
+    for a, b in ((0, 2048), (T1 // 2, T1 // 2 + 2048), (T1, T)):
+        y_iso = oracle.out_norm(o[a:b].cpu().numpy(), z[a:b].cpu().numpy(), w_h, 1e-6)
+        dist = f16_ulp_distance(y[a:b].cpu().numpy(), y_iso)
+        log("  y rows [%d,%d): max ulp %d" % (a, b, dist.max()))
+        assert dist.max() <= 1
