@@ -1,0 +1,92 @@
+"""Properties of the gfx950 code the kernels compile to (CPU only: hipcc cross-compiles).
+
+Every HIP source is compiled to assembly with the library's own flags, and the listing is
+checked for rules the design relies on:
+
+* m0 is written only by the direct global-to-LDS load sequences (`s_add_u32 m0, ...`
+  immediately before each `buffer_load_dwordx4 ... lds`): those loads take their LDS
+  address from m0 without declaring it, which is safe only while nothing else in the
+  kernels uses the register;
+* no packed FP32 vector instruction (`v_pk_add_f32`, `v_pk_mul_f32`, `v_pk_fma_f32`)
+  appears: the build disables them;
+* no scalar memory store or scalar atomic appears: every store goes through the vector
+  memory path;
+* the fused scan kernel has no scratch (register spill) traffic: its state and operands
+  stay in registers.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from linear_attention_recurrence_gated_amd import build
+
+HIPCC = build.HIPCC
+
+
+def _device_asm(src):
+    out = os.path.join(build.BUILD_DIR, os.path.basename(src) + ".s")
+    os.makedirs(build.BUILD_DIR, exist_ok=True)
+    flags = [f for f in build.FLAGS if f not in ("-fPIC",)]
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", out],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    with open(out) as f:
+        return f.read()
+
+
+def _instructions(text):
+    """(function, mnemonic, line) of every instruction of the listing."""
+    fn = None
+    for line in text.splitlines():
+        m = re.match(r"^([A-Za-z_.$][\w.$]*):", line)
+        if m and not m.group(1).startswith(".L"):
+            fn = m.group(1)
+            continue
+        s = line.strip()
+        if not s or s.startswith((";", ".", "//")) or s.endswith(":"):
+            continue
+        yield fn, s.split()[0], s
+
+
+@pytest.fixture(scope="module")
+def listings():
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    srcs = sorted(os.path.join(build.CSRC, f) for f in os.listdir(build.CSRC)
+                  if f.endswith(".hip"))
+    return {os.path.basename(s): list(_instructions(_device_asm(s))) for s in srcs}
+
+
+def test_m0_only_addressed_by_direct_loads(listings):
+    seen = 0
+    for name, ins in listings.items():
+        for i, (fn, op, line) in enumerate(ins):
+            if re.search(r"\bm0\b", line):
+                assert op == "s_add_u32" and line.split()[1] == "m0,", (name, fn, line)
+                nxt = ins[i + 1][2]
+                assert nxt.startswith("buffer_load_dwordx4") and nxt.endswith(" lds"), (name, line, nxt)
+                seen += 1
+    assert seen > 0  # the direct loads are there
+
+
+def test_no_packed_fp32_vector_instructions(listings):
+    for name, ins in listings.items():
+        bad = [line for _, op, line in ins if op in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")]
+        assert not bad, (name, bad[:3])
+
+
+def test_no_scalar_memory_writes(listings):
+    for name, ins in listings.items():
+        bad = [line for _, op, line in ins
+               if op.startswith(("s_store", "s_buffer_store", "s_scratch_store", "s_atomic",
+                                 "s_buffer_atomic", "s_dcache_wb"))]
+        assert not bad, (name, bad[:3])
+
+
+def test_fused_kernel_has_no_scratch_traffic(listings):
+    fused = [line for fn, op, line in listings["gdn_chunk.hip"]
+             if fn and "chunk_fused_kernel" in fn and op.startswith("scratch_")]
+    assert not fused, fused[:3]
