@@ -163,6 +163,26 @@ def test_zero_gate_zero_beta(kind):
 
 
 @pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_extreme_gates_and_repeated_keys(kind):
+    """Decays far outside the workload's range and a degenerate key run, across a
+    super-block boundary with a ragged tail: strong decays (e^g = e^-40), a complete reset
+    in FP32 (e^-200 underflows to 0), a chunk whose gate prefix reaches -160, no decay with
+    beta = 1 (the plain delta rule), beta = 1e-6, and 33 equal keys in a row (a WY block
+    whose Gram tile is all ones).  Every exponent the chunked form evaluates stays <= 0, so
+    nothing may overflow, and both paths must stay within their gates."""
+    x = make_inputs(2100, seed=19)
+    g, b, k = x["g"], x["beta"], x["k"]
+    g[100:140] = -40.0
+    g[500] = -200.0
+    g[1024:1056] = -5.0
+    g[1500:1600] = 0.0
+    b[1500:1600] = 1.0
+    b[600:700] = 1e-6
+    k[801:833] = k[800]
+    _check(kind, x, to_dev(x), tag="extreme")
+
+
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
 def test_other_group_sizes(kind):
     """1, 2 and 4 value heads per key head (the map h -> h mod n_k_heads)."""
     for hk, hv in ((4, 4), (8, 16), (2, 8)):
