@@ -37,16 +37,12 @@
 namespace gdn {
 namespace {
 
-constexpr int KP = 132;  // LDS row stride (floats) of a staged 32 x 128 K or Q chunk
-
 // ---------------------------------------------------------------------------------------
 // prep
 // ---------------------------------------------------------------------------------------
 constexpr int PREP_NT = 256;
 
 struct PrepSmem {
-  float k[kChunk][KP];
-  float q[kChunk][KP];
   float gram[2][kChunk][kChunk + 1];  // [0] = K K^T, [1] = Q K^T
   float gs[kMaxGroup][kChunk];
   float bs[kMaxGroup][kChunk];
@@ -63,19 +59,7 @@ __device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, Pre
   const int w = tid >> 6, l = tid & 63;
   const int c0 = c * kChunk;  // first token of the chunk, relative to the super-block
 
-  // 1. K, Q rows of the chunk (zero past the end), g and beta of the value heads.
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int f = tid + PREP_NT * m, tt = f >> 5, p = f & 31;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-    if (c0 + tt < a.n_tok) {
-      const int off = ((a.t_begin + c0 + tt) * Hk + kh) * kDim + 4 * p;
-      kv = *reinterpret_cast<const float4*>(a.k + off);
-      qv = *reinterpret_cast<const float4*>(a.q + off);
-    }
-    *reinterpret_cast<float4*>(&sm.k[tt][4 * p]) = kv;
-    *reinterpret_cast<float4*>(&sm.q[tt][4 * p]) = qv;
-  }
+  // 1. g and beta of the value heads (zero past the end).
   if (tid < kChunk * G) {
     const int m = tid >> 5, tt = tid & 31;
     float gv = 0.f, bv = 0.f;
@@ -90,20 +74,32 @@ __device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, Pre
   __syncthreads();
 
   // 2. Gram tiles on the matrix cores.  Needed: the lower-triangular 16x16 tiles
-  //    (0,0), (1,0), (1,1) of K K^T and of Q K^T; wave w takes tiles w and w + 4.
-  for (int tile = w; tile < 6; tile += 4) {
+  //    (0,0), (1,0), (1,1) of K K^T and of Q K^T; wave w takes tiles w and w + 4.  The
+  //    operands come straight from global memory into registers (lane: row l % 16, four
+  //    keys 4 (l / 16) of each group of 16): the K and Q rows of the chunk, through
+  //    descriptors whose range ends with the call's last token, so rows past it read as 0.
+  const int nv = min(kChunk, a.n_tok - c0);  // tokens of the chunk (>= 1)
+  const size_t row0 = ((size_t)(a.t_begin + c0) * Hk + kh) * kDim;
+  const uint32_t rbytes = (uint32_t)(((nv - 1) * Hk + 1) * kDim * 4);
+  const buf_rsrc rk = make_rsrc(a.k + row0, rbytes), rq = make_rsrc(a.q + row0, rbytes);
+  for (int tile = __builtin_amdgcn_readfirstlane(w); tile < 6; tile += 4) {  // (uniform)
     const int mat = tile / 3, sub = tile % 3;
     const int ti = sub == 0 ? 0 : 1, tj = sub == 2 ? 1 : 0;
-    const float* X = mat == 0 ? &sm.k[0][0] : &sm.q[0][0];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t lane_col = 16 * (l >> 4);  // bytes
+    const uint32_t offa = (uint32_t)((16 * ti + (l & 15)) * Hk * kDim * 4) + lane_col;
+    const uint32_t offb = (uint32_t)((16 * tj + (l & 15)) * Hk * kDim * 4) + lane_col;
+    const buf_rsrc ra = mat == 0 ? rk : rq;
+    f32x4 av[kDim / 16], bv[kDim / 16];
 #pragma unroll
     for (int s = 0; s < kDim / 16; ++s) {
-      const int col = 16 * s + 4 * (l >> 4);
-      const f32x4 av = *reinterpret_cast<const f32x4*>(X + (16 * ti + (l & 15)) * KP + col);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.k[16 * tj + (l & 15)][col]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc = mfma16x16x4(av[r], bv[r], acc);
+      av[s] = buf_load4(ra, offa + 64 * s);
+      bv[s] = buf_load4(rk, offb + 64 * s);
     }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kDim / 16; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = mfma16x16x4(av[s][r], bv[s][r], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       sm.gram[mat][16 * ti + 4 * (l >> 4) + r][16 * tj + (l & 15)] = acc[r];
@@ -556,7 +552,7 @@ __device__ __forceinline__ void scan_block(const ChunkArgs& a, int b, int nb, Sc
 }
 
 // Prep alone: one workgroup per (chunk, key head) of a super-block.
-__global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(PREP_NT, 4) void chunk_prep_kernel(ChunkArgs a) {
   __shared__ PrepSmem sm;
   prep_item(a, blockIdx.x, blockIdx.y, sm, threadIdx.x);
 }
