@@ -142,7 +142,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--tokens", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the CPU-oracle sample (0 disables the CPU baseline)")
