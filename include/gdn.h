@@ -137,7 +137,9 @@ int gdn_recurrence_chunked_timed(const float* q, const float* k, const float* v,
  *                          * w[h][j] * sigmoid(z[t][h][j]) )
  *
  *   o, z, w : inputs (layouts above), read only.  eps >= 0 (a negative or non-finite eps
- *             is GDN_ERR_BAD_SHAPE).
+ *             is GDN_ERR_BAD_SHAPE).  The mean of squares is accumulated in FP32, so a row
+ *             whose largest |o| exceeds about 1.6e18 overflows it (its y is then 0); an
+ *             all-zero row with eps = 0 gives NaN, as the formula does.
  *   y       : output, IEEE binary16 bit patterns, rounded to nearest even.  Must not
  *             overlap o, z or w.
  *   T = 0   : nothing is written; returns GDN_OK.

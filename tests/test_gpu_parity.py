@@ -219,6 +219,39 @@ def test_t8192_seq_and_norm():
     assert bad == 0, worst
 
 
+def test_norm_extreme_rows():
+    """The norm alone on rows far from the workload: all-zero rows (only eps remains),
+    rows of 1e-20 (their squares underflow; eps dominates), rows of 1e15 (large but with a
+    finite FP32 sum of squares), gates of +-30 and +-100 (the sigmoid saturates to 0 and
+    1), and weights of zero and of either sign.  Within 1 fp16 ulp of the oracle's norm of
+    the same FP32 rows."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    rng = np.random.default_rng(31)
+    T, Hv, dv = 40, 48, 128
+    o = rng.standard_normal((T, Hv, dv)).astype(np.float32)
+    o[0] = 0.0
+    o[1] *= np.float32(1e-20)
+    o[2] *= np.float32(1e15)
+    o[3, :24] = 0.0
+    z = rng.standard_normal((T, Hv, dv)).astype(np.float32)
+    z[4:8] = np.array([-100.0, -30.0, 30.0, 100.0], np.float32)[:, None, None]
+    z[8, :, ::2] = -100.0
+    w = (1.0 + 0.5 * rng.standard_normal((Hv, dv))).astype(np.float32)
+    w[:, :8] = 0.0
+    w[:, 8:16] *= -1.0
+    d = {n: torch.from_numpy(a).cuda() for n, a in (("o", o), ("z", z), ("w", w))}
+    y = gdn.out_norm(d["o"], d["z"], d["w"], eps=1e-6)
+    torch.cuda.synchronize()
+    y_h = y.cpu().numpy()
+    y_ref = oracle.out_norm(o, z, w, 1e-6)
+    assert np.isfinite(y_h.astype(np.float32)).all()
+    dist = f16_ulp_distance(y_h, y_ref)
+    log("norm extreme rows: max ulp %d, exact %.4f" % (dist.max(), (dist == 0).mean()))
+    assert dist.max() <= 1
+    assert not y_h[0].any() and not y_h[1].any()  # zero and underflowing rows give 0
+
+
 def test_t32768_chunked_and_seq():
     """One layer, T = 32768: 16 super-blocks of 2048 tokens in one chunked call, the state
     carried between them; the sequential kernel beside it.  Six value heads are checked
