@@ -8,11 +8,12 @@
 //
 // Work split (designed for wave64 and 256 CUs, not taken from the pages):
 //  - one workgroup = one key head x 8 value columns, for all value heads of that key head
-//    (so every q/k value read from LDS feeds G heads); 16 key heads x 16 column blocks =
+//    (the G heads share every staged tile of q/k rows); 16 key heads x 16 column blocks =
 //    256 workgroups, one per CU;
-//  - a 64-lane wave holds 2 value columns; the 32 lanes of a column each own 4 of the 128
-//    key rows of G state columns (4G floats of state per lane, in VGPRs for the whole
-//    sequence);
+//  - a 64-lane wave holds 2 value columns of one value head; the 32 lanes of a column each
+//    own 4 of the 128 key rows (4 floats of state per lane, in VGPRs for the whole
+//    sequence); the G value heads of the key head are G groups of 4 waves, so every SIMD
+//    runs G waves whose dependency chains interleave;
 //  - the kv and output sums over the 128 rows are reduced across the 32 lanes with four
 //    DPP steps and one ds_swizzle (lane ^ 16), entirely inside the wave: no LDS array and
 //    no barrier per token;
@@ -27,7 +28,7 @@ namespace {
 
 constexpr int TB = 16;    // tokens per staged tile
 constexpr int COLS = 8;   // value columns per workgroup
-constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int NT = 256;   // threads per value head (4 waves); a workgroup has G NT
 constexpr int NCB = kDim / COLS;  // column blocks per key head
 
 template <int G>
@@ -52,12 +53,14 @@ __device__ __forceinline__ void stage_load(SeqStage& st, const SeqArgs& a, int t
                                            int cb, int tid) {
   const int Hk = a.n_k_heads, Hv = G * a.n_k_heads;
   const int p = tid & 31;
+  if (tid < NT) {  // whole waves
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int t = min(t0 + (tid >> 5) + 8 * m, a.T - 1);  // clamped rows are never used
-    const int off = (t * Hk + kh) * kDim + 4 * p;
-    st.k[m] = *reinterpret_cast<const float4*>(a.k + off);
-    st.q[m] = *reinterpret_cast<const float4*>(a.q + off);
+    for (int m = 0; m < 2; ++m) {
+      const int t = min(t0 + (tid >> 5) + 8 * m, a.T - 1);  // clamped rows are never used
+      const int off = (t * Hk + kh) * kDim + 4 * p;
+      st.k[m] = *reinterpret_cast<const float4*>(a.k + off);
+      st.q[m] = *reinterpret_cast<const float4*>(a.q + off);
+    }
   }
   if (tid < TB * G * 2) {
     const int tt = tid / (2 * G), rem = tid % (2 * G), m = rem >> 1, half = rem & 1;
@@ -78,22 +81,24 @@ template <int G>
 __device__ __forceinline__ void stage_store(SeqSmem<G>& sm, int buf, const SeqStage& st,
                                             int tid) {
   const int p = tid & 31;
-  float part[2];
+  if (tid < NT) {  // whole waves
+    float part[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int tt = (tid >> 5) + 8 * m;
-    *reinterpret_cast<float4*>(&sm.k[buf][tt][4 * p]) = st.k[m];
-    *reinterpret_cast<float4*>(&sm.q[buf][tt][4 * p]) = st.q[m];
-    // explicit fused operations: the prologue's copy of this code and the loop's must
-    // evaluate k.q alike (left to the compiler, they may be contracted differently)
-    part[m] = fmaf(st.k[m].w, st.q[m].w,
-                   fmaf(st.k[m].z, st.q[m].z, fmaf(st.k[m].y, st.q[m].y, st.k[m].x * st.q[m].x)));
-  }
-  // each half-wave holds one token's k and q rows
+    for (int m = 0; m < 2; ++m) {
+      const int tt = (tid >> 5) + 8 * m;
+      *reinterpret_cast<float4*>(&sm.k[buf][tt][4 * p]) = st.k[m];
+      *reinterpret_cast<float4*>(&sm.q[buf][tt][4 * p]) = st.q[m];
+      // explicit fused operations: the prologue's copy of this code and the loop's must
+      // evaluate k.q alike (left to the compiler, they may be contracted differently)
+      part[m] = fmaf(st.k[m].w, st.q[m].w,
+                     fmaf(st.k[m].z, st.q[m].z, fmaf(st.k[m].y, st.q[m].y, st.k[m].x * st.q[m].x)));
+    }
+    // each half-wave holds one token's k and q rows
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const float s = half_wave_sum(part[m]);
-    if (p == 0) sm.kq[buf][(tid >> 5) + 8 * m] = s;
+    for (int m = 0; m < 2; ++m) {
+      const float s = half_wave_sum(part[m]);
+      if (p == 0) sm.kq[buf][(tid >> 5) + 8 * m] = s;
+    }
   }
   if (tid < TB * G * 2) {
     const int tt = tid / (2 * G), rem = tid % (2 * G), m = rem >> 1, half = rem & 1;
@@ -119,55 +124,51 @@ __device__ __forceinline__ void store_outputs(const SeqSmem<G>& sm, int buf, con
 }
 
 template <int G>
-__device__ __forceinline__ void compute_tile(SeqSmem<G>& sm, int buf, int ntok,
-                                             float (&S)[G][4], int r, int cl) {
+__device__ __forceinline__ void compute_tile(SeqSmem<G>& sm, int buf, int ntok, float (&S)[4],
+                                             int m, int r, int cl) {
+  // The k and q rows of the next token are read while this one computes, and every
+  // per-token scalar is read before the reductions: no LDS latency waits on the chain.
+  float4 kk = *reinterpret_cast<const float4*>(&sm.k[buf][0][4 * r]);
+  float4 qq = *reinterpret_cast<const float4*>(&sm.q[buf][0][4 * r]);
   for (int tt = 0; tt < ntok; ++tt) {
-    const float4 kk = *reinterpret_cast<const float4*>(&sm.k[buf][tt][4 * r]);
-    const float4 qq = *reinterpret_cast<const float4*>(&sm.q[buf][tt][4 * r]);
-    float pk[G], pq[G];
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-      pk[m] = fmaf(S[m][3], kk.w, fmaf(S[m][2], kk.z, fmaf(S[m][1], kk.y, S[m][0] * kk.x)));
-      pq[m] = fmaf(S[m][3], qq.w, fmaf(S[m][2], qq.z, fmaf(S[m][1], qq.y, S[m][0] * qq.x)));
-    }
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-      pk[m] = half_wave_sum(pk[m]);  // S^T k over the 128 rows of this column
-      pq[m] = half_wave_sum(pq[m]);  // S^T q
-    }
+    const int tn = min(tt + 1, ntok - 1);  // the last token of the tile re-reads its own
+    const float4 kn = *reinterpret_cast<const float4*>(&sm.k[buf][tn][4 * r]);
+    const float4 qn = *reinterpret_cast<const float4*>(&sm.q[buf][tn][4 * r]);
+    const float2 ab = sm.ab[buf][tt][m];
+    const float vv = sm.v[buf][tt][m][cl];
     const float kq = sm.kq[buf][tt];
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-      const float2 ab = sm.ab[buf][tt][m];
-      const float vv = sm.v[buf][tt][m][cl];
-      const float d = ab.y * fmaf(-ab.x, pk[m], vv);  // beta (v - e^g S^T k)
-      const float om = fmaf(ab.x, pq[m], d * kq);     // (e^g S + k d^T)^T q
-      S[m][0] = fmaf(kk.x, d, ab.x * S[m][0]);
-      S[m][1] = fmaf(kk.y, d, ab.x * S[m][1]);
-      S[m][2] = fmaf(kk.z, d, ab.x * S[m][2]);
-      S[m][3] = fmaf(kk.w, d, ab.x * S[m][3]);
-      if (r == m) sm.o[buf][tt][m][cl] = om;
-    }
+    float pk = fmaf(S[3], kk.w, fmaf(S[2], kk.z, fmaf(S[1], kk.y, S[0] * kk.x)));
+    float pq = fmaf(S[3], qq.w, fmaf(S[2], qq.z, fmaf(S[1], qq.y, S[0] * qq.x)));
+    pk = half_wave_sum(pk);  // S^T k over the 128 rows of this column
+    pq = half_wave_sum(pq);  // S^T q
+    const float d = ab.y * fmaf(-ab.x, pk, vv);  // beta (v - e^g S^T k)
+    const float om = fmaf(ab.x, pq, d * kq);     // (e^g S + k d^T)^T q
+    S[0] = fmaf(kk.x, d, ab.x * S[0]);
+    S[1] = fmaf(kk.y, d, ab.x * S[1]);
+    S[2] = fmaf(kk.z, d, ab.x * S[2]);
+    S[3] = fmaf(kk.w, d, ab.x * S[3]);
+    if (r == 0) sm.o[buf][tt][m][cl] = om;
+    kk = kn;
+    qq = qn;
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(NT) void seq_kernel(SeqArgs a) {
+__global__ __launch_bounds__(NT * G) void seq_kernel(SeqArgs a) {
   __shared__ SeqSmem<G> sm;
   const int L = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int kh = L / NCB, cb = L % NCB;
   const int Hk = a.n_k_heads;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int cl = (tid >> 6) * 2 + (lane >> 5);  // column of this lane within the block
-  const int r = lane & 31;                       // owns key rows 4r .. 4r+3
+  const int m = __builtin_amdgcn_readfirstlane(tid / NT);  // value head of the group
+  const int cl = ((tid % NT) >> 6) * 2 + (lane >> 5);    // column of this lane in the block
+  const int r = lane & 31;                                // owns key rows 4r .. 4r+3
   const int j = cb * COLS + cl;
+  const int h = kh + m * Hk;
 
-  float S[G][4];
+  float S[4];
 #pragma unroll
-  for (int m = 0; m < G; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[m][i] = a.s_in[((kh + m * Hk) * kDim + 4 * r + i) * kDim + j];
+  for (int i = 0; i < 4; ++i) S[i] = a.s_in[(h * kDim + 4 * r + i) * kDim + j];
 
   const int ntiles = (a.T + TB - 1) / TB;
   SeqStage st;
@@ -179,24 +180,21 @@ __global__ __launch_bounds__(NT) void seq_kernel(SeqArgs a) {
     const bool more = n + 1 < ntiles;
     if (more) stage_load<G>(st, a, (n + 1) * TB, kh, cb, tid);
     if (n > 0) store_outputs<G>(sm, buf ^ 1, a, (n - 1) * TB, kh, cb, tid);
-    compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, r, cl);
+    compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, m, r, cl);
     if (more) stage_store<G>(sm, buf ^ 1, st, tid);
     __syncthreads();
   }
   store_outputs<G>(sm, (ntiles - 1) & 1, a, (ntiles - 1) * TB, kh, cb, tid);
 
 #pragma unroll
-  for (int m = 0; m < G; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a.s_out[((kh + m * Hk) * kDim + 4 * r + i) * kDim + j] = S[m][i];
+  for (int i = 0; i < 4; ++i) a.s_out[(h * kDim + 4 * r + i) * kDim + j] = S[i];
 }
 
 template <int G>
 hipError_t launch_g(const SeqArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<SeqArgs*>(&a)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&seq_kernel<G>),
-                         dim3(a.n_k_heads * NCB), dim3(NT), args, 0, stream);
+                         dim3(a.n_k_heads * NCB), dim3(NT * G), args, 0, stream);
 }
 
 }  // namespace
