@@ -584,37 +584,67 @@ __device__ __forceinline__ void norm_role(const NormArgs& n, int worker, int nwo
   const uint32_t bytes = (uint32_t)n.n_rows * kDim * 4;
   const buf_rsrc ro = make_rsrc(n.o, bytes), rz = make_rsrc(n.z, bytes);
   const buf_rsrc ry = make_rsrc(n.y, bytes / 2);
-  f32x4 ov[2][2], zv[2][2];  // [buffer][row of the slice]
+  const buf_rsrc rw = make_rsrc(n.w, (uint32_t)n.n_v_heads * kDim * 4);
+  f32x4 ov[2][2], zv[2][2], wv[2][2];  // [buffer][row of the slice]
   auto row_of = [&](int j) { return worker + j * nworkers; };
-  auto load = [&](int buf, int c) {  // rows past the end read as 0
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t off = ((uint32_t)row_of(c + kChunksPerSB * i) * kDim + 4 * p) * 4;
-      ov[buf][i] = buf_load4(ro, off);
-      zv[buf][i] = buf_load4(rz, off);
-    }
-  };
-  auto finish = [&](int buf, int c) {
+  // Buffer indices are compile-time constants throughout, and the loops have no early
+  // exit: loaded values in flight never meet a branch join, at which the compiler would
+  // have to wait for them.
+  auto load = [&](auto bc, int c) {  // rows past the end read as 0
+    constexpr int B = decltype(bc)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = row_of(c + kChunksPerSB * i);
-      if (r < n.n_rows) {  // whole half-waves: the two halves of a wave may differ
-        const float4 wv =
-            *reinterpret_cast<const float4*>(n.w + (r % n.n_v_heads) * kDim + 4 * p);
-        buf_store2(ry, ((uint32_t)r * kDim + 4 * p) * 2,
-                   gated_rms_row(ov[buf][i], zv[buf][i], wv, n.eps));
-      }
+      const uint32_t off = ((uint32_t)r * kDim + 4 * p) * 4;
+      ov[B][i] = buf_load4(ro, off);
+      zv[B][i] = buf_load4(rz, off);
+      wv[B][i] = buf_load4(rw, ((uint32_t)(r % n.n_v_heads) * kDim + 4 * p) * 4);
     }
   };
-  load(0, 0);
+  auto finish = [&](auto bc, int c) {
+    constexpr int B = decltype(bc)::value;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = row_of(c + kChunksPerSB * i);
+      if (r < n.n_rows)  // whole half-waves: the two halves of a wave may differ
+        buf_store2(ry, ((uint32_t)r * kDim + 4 * p) * 2,
+                   gated_rms_row(ov[B][i], zv[B][i],
+                                 float4{wv[B][i][0], wv[B][i][1], wv[B][i][2], wv[B][i][3]},
+                                 n.eps));
+    }
+  };
+  // Slices j .. 63 after the chunks (no barriers), the loads of slice j already in buffer B.
+  auto tail = [&](auto bc, int j) {
+    if constexpr (decltype(bc)::value == 1) {
+      load(ic<0>(), j + 1);
+      finish(ic<1>(), j);
+      ++j;
+    }
+    for (; j < kChunksPerSB; j += 2) {
+      load(ic<1>(), j + 1);
+      finish(ic<0>(), j);
+      load(ic<0>(), j + 2);
+      finish(ic<1>(), j + 1);
+    }
+  };
+  load(ic<0>(), 0);
   barrier_only();
-  for (int c = 0; c < kChunksPerSB; c += 2) {
-    load(1, c + 1);
-    finish(0, c);
-    if (c < nch) barrier_only();
-    if (c + 2 < kChunksPerSB) load(0, c + 2);
-    finish(1, c + 1);
-    if (c + 1 < nch) barrier_only();
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    load(ic<1>(), c + 1);
+    finish(ic<0>(), c);
+    barrier_only();
+    load(ic<0>(), c + 2);
+    finish(ic<1>(), c + 1);
+    barrier_only();
+  }
+  if (c < nch) {  // an odd chunk count: one more chunk, then the rest from buffer 1
+    load(ic<1>(), c + 1);
+    finish(ic<0>(), c);
+    barrier_only();
+    tail(ic<1>(), c + 1);
+  } else {
+    tail(ic<0>(), c);
   }
   barrier_only();  // the compute waves' last exchange
 }
