@@ -119,14 +119,23 @@ def chunked_workspace_bytes(n_k_heads, n_v_heads, dk=128, dv=128):
 _workspaces = {}
 
 
-def workspace(device, n_k_heads, n_v_heads, dk=128, dv=128):
-    """The chunked kernels' scratch: allocated once per device on first use and kept."""
+def workspace(device, n_k_heads, n_v_heads, dk=128, dv=128, stream=None):
+    """The chunked kernels' scratch, one per (device, stream): allocated on first use and
+    kept.  Calls on one stream are ordered, so they can share it; calls on different
+    streams may overlap, so each stream gets its own (calls that pass a workspace
+    themselves must not share one across streams either)."""
     need = chunked_workspace_bytes(n_k_heads, n_v_heads, dk, dv)
     dev = torch.device(device)
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    key = (dev.index, s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        if ws is not None:
+            s.synchronize()  # work already queued on this stream may still use the old one
+        with torch.cuda.stream(s):  # the allocator ties the memory to the stream it serves
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -145,7 +154,7 @@ def recurrence_chunked(q, k, v, g, beta, state_in, state_out=None, o=None, ws=No
         o = torch.empty_like(v)
     _f32(state_out, "state_out"); _f32(o, "o")
     if ws is None:
-        ws = workspace(q.device, Hk, Hv, dk, dv)
+        ws = workspace(q.device, Hk, Hv, dk, dv, stream)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out),
             _ptr(o), T, Hk, Hv, dk, dv, _ptr(ws), ws.numel() * ws.element_size())
     if scan_events is None:
@@ -174,7 +183,7 @@ def recurrence(q, k, v, g, beta, state_in, state_out=None, o=None, ws=None, stre
         o = torch.empty_like(v)
     _f32(state_out, "state_out"); _f32(o, "o")
     if ws is None and T >= CHUNKED_MIN_T:
-        ws = workspace(q.device, Hk, Hv, dk, dv)
+        ws = workspace(q.device, Hk, Hv, dk, dv, stream)
     ws_ptr, ws_bytes = (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
     st = lib().gdn_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
                               _ptr(state_out), _ptr(o), T, Hk, Hv, dk, dv, ws_ptr, ws_bytes,
@@ -202,7 +211,7 @@ def layer_chunked(q, k, v, g, beta, state_in, z, w, eps=1e-6, state_out=None, o=
     if y.dtype != torch.float16 or not y.is_contiguous() or not y.is_cuda:
         raise TypeError("y must be a contiguous float16 CUDA tensor")
     if ws is None:
-        ws = workspace(q.device, Hk, Hv, dk, dv)
+        ws = workspace(q.device, Hk, Hv, dk, dv, stream)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out),
             _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(y), T, Hk, Hv, dk, dv, _ptr(ws),
             ws.numel() * ws.element_size())

@@ -141,6 +141,33 @@ def test_split_calls_bitwise(kind, T, T1):
     assert torch.equal(o.view(torch.int32), torch.cat(parts).view(torch.int32))
     assert torch.equal(s.view(torch.int32), st.view(torch.int32))
 
+def test_concurrent_streams_default_workspaces():
+    """Layer calls on two streams at once, each with the binding's default workspace (one
+    per stream), give the bits of the same calls made one after the other."""
+    from linear_attention_recurrence_gated_amd import gdn
+    calls = []
+    for T, seed in ((4100, 41), (3000, 42)):
+        x = make_inputs(T, seed=seed, with_norm=True)
+        calls.append(to_dev(x))
+
+    def layer(d, stream=None):
+        return gdn.layer_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"],
+                                 d["w"], stream=stream)
+
+    ref = [layer(d) for d in calls]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = []
+    for s, d in zip(streams, calls):
+        with torch.cuda.stream(s):
+            got.append(layer(d, stream=s))
+    torch.cuda.synchronize()
+    for r, g in zip(ref, got):
+        for a, b in zip(r, g):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.float16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.float16 else b.view(torch.int32))
+
+
 @pytest.mark.parametrize("kind", ["seq", "chunked"])
 def test_zero_tokens_copies_state(kind):
     x = make_inputs(4, seed=1)
