@@ -102,7 +102,9 @@ size_t gdn_chunked_workspace_bytes(int n_k_heads, int n_v_heads, int dk, int dv)
  *   workspace, workspace_bytes : device scratch of at least
  *                      gdn_chunked_workspace_bytes(...) bytes, 16-byte aligned.  Its
  *                      contents on entry do not matter and on return are unspecified.
- *                      It must not overlap any input or output.
+ *                      It must not overlap any input or output.  The call uses it until
+ *                      its work on `stream` has finished: calls that may run at the same
+ *                      time (on different streams) need workspaces of their own.
  *   Other arguments, aliasing rules and T = 0 behave as for gdn_recurrence_seq.
  *   Results differ from gdn_recurrence_seq only by float32 summation order.
  */
