@@ -138,6 +138,79 @@ def cpu_baseline(x, tokens):
                       "gated RMS norm (%.1f s wall)" % (tokens, dt)}
 
 
+def _median(xs):
+    return sorted(xs)[len(xs) // 2]
+
+
+def context_workloads(gdn, d, hip, stream, dev, runs=3):
+    """Times (HIP events on the launch stream, medians of `runs` after one unmeasured run)
+    of the T = 8192 sequential layer and of the 36-layer stack at T = 2048.  The stack's
+    layers get inputs of their own, drawn on the device with the distributions of
+    make_inputs (their values do not change the work), so no layer finds another's data
+    in the caches."""
+    import torch
+    out = {}
+    T8 = min(8192, d["q"].shape[0])
+    sl = {n: (d[n][:T8] if n not in ("s0", "w") else d[n]) for n in d}
+    o8 = torch.empty_like(sl["v"])
+    s8 = torch.empty_like(sl["s0"])
+    y8 = torch.empty(sl["v"].shape, dtype=torch.float16, device=dev)
+    rec, lay = [], []
+    for i in range(runs + 1):
+        evs = hip.create(3)
+        hip.record(evs[0], stream.cuda_stream)
+        gdn.recurrence_seq(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["s0"],
+                           state_out=s8, o=o8)
+        hip.record(evs[1], stream.cuda_stream)
+        gdn.out_norm(o8, sl["z"], sl["w"], eps=1e-6, y=y8)
+        hip.record(evs[2], stream.cuda_stream)
+        torch.cuda.synchronize()
+        if i:
+            rec.append(hip.elapsed_ms(evs[0], evs[1]))
+            lay.append(hip.elapsed_ms(evs[0], evs[2]))
+        hip.destroy(evs)
+    out["seq_recurrence_T8192_us_per_token"] = round(_median(rec) * 1e3 / T8, 6)
+    out["seq_layer_T8192_us_per_token"] = round(_median(lay) * 1e3 / T8, 6)
+    del o8, s8, y8
+
+    L, T2, Hk, Hv, D = 36, 2048, 16, 48, 128
+    gen = torch.Generator(device=dev)
+    layers = []
+    for l in range(L):
+        gen.manual_seed(1000 + l)
+        q = torch.randn(T2, Hk, D, device=dev, generator=gen)
+        q = q / q.norm(dim=-1, keepdim=True) / D ** 0.5
+        k = torch.randn(T2, Hk, D, device=dev, generator=gen)
+        k = k / k.norm(dim=-1, keepdim=True)
+        v = torch.randn(T2, Hv, D, device=dev, generator=gen)
+        g = -torch.exp(torch.rand(T2, Hv, device=dev, generator=gen) * -4.0)
+        beta = torch.sigmoid(torch.randn(T2, Hv, device=dev, generator=gen))
+        s0 = 0.1 * torch.randn(Hv, D, D, device=dev, generator=gen)
+        w = 1.0 + 0.1 * torch.randn(Hv, D, device=dev, generator=gen)
+        z = torch.randn(T2, Hv, D, device=dev, generator=gen)
+        layers.append(dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0, w=w, z=z,
+                           st=torch.empty_like(s0), o=torch.empty_like(v),
+                           y=torch.empty(v.shape, dtype=torch.float16, device=dev)))
+    ws = gdn.workspace(dev, Hk, Hv)
+    stack = []
+    for i in range(runs + 1):
+        evs = hip.create(2)
+        hip.record(evs[0], stream.cuda_stream)
+        for t in layers:
+            gdn.layer_chunked(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], t["z"], t["w"],
+                              eps=1e-6, state_out=t["st"], o=t["o"], y=t["y"], ws=ws)
+        hip.record(evs[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        if i:
+            stack.append(hip.elapsed_ms(evs[0], evs[1]))
+        hip.destroy(evs)
+    out["stack36_T2048_ms"] = round(_median(stack), 4)
+    out["stack36_T2048_us_per_token_layer"] = round(_median(stack) * 1e3 / (L * T2), 6)
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +316,11 @@ def main():
     seq_ms = hip.elapsed_ms(evs[0], evs[1])
     hip.destroy(evs)
 
+    # The other timed workloads of the same family, for context: one layer of 8192 tokens
+    # on the sequential kernel plus the norm, and a stack of 36 independent layers of 2048
+    # tokens (recurrence + norm per layer, timed end to end).
+    ctx = context_workloads(gdn, d, hip, stream, dev)
+
     if args.calibration_copy:
         calibration_copy()
 
@@ -294,6 +372,7 @@ def main():
             "standalone_norm_hbm_frac": round(NORM_BYTES_PER_TOKEN * T / (norm_avg_ms * 1e-3)
                                               / 1e9 / PEAK_HBM_GBS, 4),
             "seq_recurrence_us_per_token": round(seq_ms * 1e3 / T, 6),
+            **ctx,
             "outputs_finite": y_ok,
         },
         "cpu_baseline": cpu,
