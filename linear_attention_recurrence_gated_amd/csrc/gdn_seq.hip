@@ -10,13 +10,13 @@
 //  - one workgroup = one key head x 8 value columns, for all value heads of that key head
 //    (the G heads share every staged tile of q/k rows); 16 key heads x 16 column blocks =
 //    256 workgroups, one per CU;
-//  - a 64-lane wave holds 2 value columns of one value head; the 32 lanes of a column each
-//    own 4 of the 128 key rows (4 floats of state per lane, in VGPRs for the whole
-//    sequence); the G value heads of the key head are G groups of 4 waves, so every SIMD
-//    runs G waves whose dependency chains interleave;
-//  - the kv and output sums over the 128 rows are reduced across the 32 lanes with four
-//    DPP steps and one ds_swizzle (lane ^ 16), entirely inside the wave: no LDS array and
-//    no barrier per token;
+//  - a 64-lane wave holds 4 value columns of one value head; the 16 lanes of a column (one
+//    DPP row) each own 8 of the 128 key rows (8 floats of state per lane, in VGPRs for the
+//    whole sequence); each value head of the key head has 2 waves, so the SIMDs run
+//    several waves whose dependency chains interleave;
+//  - the kv and output sums over the 128 rows are two chains of four products per lane,
+//    then four DPP steps across the 16 lanes of the row, entirely inside the wave: no LDS
+//    round trip, no barrier per token;
 //  - the inputs of 16 tokens (q/k rows of the key head, the block's v columns, e^{g},
 //    beta and k.q) are staged in double-buffered LDS; the next tile's global loads are in
 //    flight while the current tile computes; one barrier per 16 tokens.
@@ -28,7 +28,10 @@ namespace {
 
 constexpr int TB = 16;    // tokens per staged tile
 constexpr int COLS = 8;   // value columns per workgroup
-constexpr int NT = 256;   // threads per value head (4 waves); a workgroup has G NT
+constexpr int NT = 256;   // threads that stage the q/k rows
+constexpr int RPL = 8;    // key rows per lane: 16 lanes per column
+template <int G>
+constexpr int seq_threads() { return 128 * (G < 2 ? 2 : G); }  // 2 waves per value head
 constexpr int NCB = kDim / COLS;  // column blocks per key head
 
 template <int G>
@@ -123,52 +126,67 @@ __device__ __forceinline__ void store_outputs(const SeqSmem<G>& sm, int buf, con
   }
 }
 
+// Sum over the 16 lanes of each DPP row; every lane receives its row's sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<DPP_XOR1>(x);
+  x += dpp_mov<DPP_XOR2>(x);
+  x += dpp_mov<DPP_HALF_MIRROR>(x);
+  x += dpp_mov<DPP_MIRROR>(x);
+  return x;
+}
+
 template <int G>
-__device__ __forceinline__ void compute_tile(SeqSmem<G>& sm, int buf, int ntok, float (&S)[4],
+__device__ __forceinline__ void compute_tile(SeqSmem<G>& sm, int buf, int ntok, float (&S)[RPL],
                                              int m, int r, int cl) {
   // The k and q rows of the next token are read while this one computes, and every
   // per-token scalar is read before the reductions: no LDS latency waits on the chain.
-  float4 kk = *reinterpret_cast<const float4*>(&sm.k[buf][0][4 * r]);
-  float4 qq = *reinterpret_cast<const float4*>(&sm.q[buf][0][4 * r]);
+  const float4* kr = reinterpret_cast<const float4*>(&sm.k[buf][0][RPL * r]);
+  const float4* qr = reinterpret_cast<const float4*>(&sm.q[buf][0][RPL * r]);
+  constexpr int ROW4 = kDim / 4;  // float4 per token row
+  float4 k0 = kr[0], k1 = kr[1], q0 = qr[0], q1 = qr[1];
   for (int tt = 0; tt < ntok; ++tt) {
     const int tn = min(tt + 1, ntok - 1);  // the last token of the tile re-reads its own
-    const float4 kn = *reinterpret_cast<const float4*>(&sm.k[buf][tn][4 * r]);
-    const float4 qn = *reinterpret_cast<const float4*>(&sm.q[buf][tn][4 * r]);
+    const float4 kn0 = kr[tn * ROW4], kn1 = kr[tn * ROW4 + 1];
+    const float4 qn0 = qr[tn * ROW4], qn1 = qr[tn * ROW4 + 1];
     const float2 ab = sm.ab[buf][tt][m];
     const float vv = sm.v[buf][tt][m][cl];
     const float kq = sm.kq[buf][tt];
-    float pk = fmaf(S[3], kk.w, fmaf(S[2], kk.z, fmaf(S[1], kk.y, S[0] * kk.x)));
-    float pq = fmaf(S[3], qq.w, fmaf(S[2], qq.z, fmaf(S[1], qq.y, S[0] * qq.x)));
-    pk = half_wave_sum(pk);  // S^T k over the 128 rows of this column
-    pq = half_wave_sum(pq);  // S^T q
+    const float kk[RPL] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const float qq[RPL] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    // two chains of four products each, then the 16 lanes of the column
+    float pk = fmaf(S[3], kk[3], fmaf(S[2], kk[2], fmaf(S[1], kk[1], S[0] * kk[0]))) +
+               fmaf(S[7], kk[7], fmaf(S[6], kk[6], fmaf(S[5], kk[5], S[4] * kk[4])));
+    float pq = fmaf(S[3], qq[3], fmaf(S[2], qq[2], fmaf(S[1], qq[1], S[0] * qq[0]))) +
+               fmaf(S[7], qq[7], fmaf(S[6], qq[6], fmaf(S[5], qq[5], S[4] * qq[4])));
+    pk = row16_sum(pk);  // S^T k over the 128 rows of this column
+    pq = row16_sum(pq);  // S^T q
     const float d = ab.y * fmaf(-ab.x, pk, vv);  // beta (v - e^g S^T k)
     const float om = fmaf(ab.x, pq, d * kq);     // (e^g S + k d^T)^T q
-    S[0] = fmaf(kk.x, d, ab.x * S[0]);
-    S[1] = fmaf(kk.y, d, ab.x * S[1]);
-    S[2] = fmaf(kk.z, d, ab.x * S[2]);
-    S[3] = fmaf(kk.w, d, ab.x * S[3]);
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) S[i] = fmaf(kk[i], d, ab.x * S[i]);
     if (r == 0) sm.o[buf][tt][m][cl] = om;
-    kk = kn;
-    qq = qn;
+    k0 = kn0; k1 = kn1; q0 = qn0; q1 = qn1;
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(NT * G) void seq_kernel(SeqArgs a) {
+__global__ __launch_bounds__(seq_threads<G>()) void seq_kernel(SeqArgs a) {
   __shared__ SeqSmem<G> sm;
   const int L = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int kh = L / NCB, cb = L % NCB;
   const int Hk = a.n_k_heads;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int m = __builtin_amdgcn_readfirstlane(tid / NT);  // value head of the group
-  const int cl = ((tid % NT) >> 6) * 2 + (lane >> 5);    // column of this lane in the block
-  const int r = lane & 31;                                // owns key rows 4r .. 4r+3
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool computes = w < 2 * G;             // (G = 1: waves 2 and 3 only stage)
+  const int m = computes ? w >> 1 : 0;         // value head of the group
+  const int cl = (w & 1) * 4 + (lane >> 4);    // column of this lane in the block
+  const int r = lane & 15;                     // owns key rows 8r .. 8r+7
   const int j = cb * COLS + cl;
   const int h = kh + m * Hk;
 
-  float S[4];
+  float S[RPL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) S[i] = a.s_in[(h * kDim + 4 * r + i) * kDim + j];
+  for (int i = 0; i < RPL; ++i) S[i] = a.s_in[(h * kDim + RPL * r + i) * kDim + j];
 
   const int ntiles = (a.T + TB - 1) / TB;
   SeqStage st;
@@ -180,21 +198,23 @@ __global__ __launch_bounds__(NT * G) void seq_kernel(SeqArgs a) {
     const bool more = n + 1 < ntiles;
     if (more) stage_load<G>(st, a, (n + 1) * TB, kh, cb, tid);
     if (n > 0) store_outputs<G>(sm, buf ^ 1, a, (n - 1) * TB, kh, cb, tid);
-    compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, m, r, cl);
+    if (computes) compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, m, r, cl);
     if (more) stage_store<G>(sm, buf ^ 1, st, tid);
     __syncthreads();
   }
   store_outputs<G>(sm, (ntiles - 1) & 1, a, (ntiles - 1) * TB, kh, cb, tid);
 
+  if (computes) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a.s_out[(h * kDim + 4 * r + i) * kDim + j] = S[i];
+    for (int i = 0; i < RPL; ++i) a.s_out[(h * kDim + RPL * r + i) * kDim + j] = S[i];
+  }
 }
 
 template <int G>
 hipError_t launch_g(const SeqArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<SeqArgs*>(&a)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&seq_kernel<G>),
-                         dim3(a.n_k_heads * NCB), dim3(NT * G), args, 0, stream);
+                         dim3(a.n_k_heads * NCB), dim3(seq_threads<G>()), args, 0, stream);
 }
 
 }  // namespace

@@ -168,7 +168,7 @@ def recurrence_chunked(q, k, v, g, beta, state_in, state_out=None, o=None, ws=No
     return o, state_out
 
 
-CHUNKED_MIN_T = 48  # GDN_CHUNKED_MIN_T of gdn.h
+CHUNKED_MIN_T = 56  # GDN_CHUNKED_MIN_T of gdn.h
 
 
 def recurrence(q, k, v, g, beta, state_in, state_out=None, o=None, ws=None, stream=None):

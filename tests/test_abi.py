@@ -174,11 +174,11 @@ def _auto(L, a, T=64, Hk=16, Hv=48, ws_bytes=None):
 
 
 def test_auto_dispatch_validation(L):
-    """gdn_recurrence validates as the kernel it picks: from 48 tokens on the chunked path
+    """gdn_recurrence validates as the kernel it picks: from 56 tokens on the chunked path
     (which needs the workspace), below that the sequential one (which does not)."""
     a = _addrs()
     assert _auto(L, dict(a, ws=0), T=64) == WS
-    assert _auto(L, a, T=48, ws_bytes=1024) == WS
+    assert _auto(L, a, T=56, ws_bytes=1024) == WS
     assert _auto(L, dict(a, q=0), T=16) == NULLP
     assert _auto(L, dict(a, o=a["q"]), T=8) == ALIAS
     assert _auto(L, a, T=16, Hv=40) == SHAPE

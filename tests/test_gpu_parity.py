@@ -366,10 +366,10 @@ def test_layer_t32768_against_oracle():
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("T", [5, 32, 47, 48, 100])
+@pytest.mark.parametrize("T", [5, 32, 55, 56, 100])
 def test_auto_dispatch(T):
-    """gdn_recurrence gives the sequential kernel's bits below 48 tokens and the chunked
-    path's from 48 on."""
+    """gdn_recurrence gives the sequential kernel's bits below 56 tokens and the chunked
+    path's from 56 on."""
     from linear_attention_recurrence_gated_amd import gdn
     x = make_inputs(T, seed=9)
     d = to_dev(x)
