@@ -366,6 +366,52 @@ def test_layer_t32768_against_oracle():
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+def test_layer_extreme_inputs():
+    """The one-call layer on the extreme decays, betas and repeated keys of the recurrence
+    test, with saturated gates z = +-60 on some tokens: o and the state within the chunked
+    gate, y within the end-to-end bound of the oracle's norm of the oracle's output."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    x = make_inputs(2100, seed=23, with_norm=True)
+    g, b, k, z = x["g"], x["beta"], x["k"], x["z"]
+    g[100:140] = -40.0
+    g[500] = -200.0
+    g[1024:1056] = -5.0
+    g[1500:1600] = 0.0
+    b[1500:1600] = 1.0
+    b[600:700] = 1e-6
+    k[801:833] = k[800]
+    z[2000:2010] = 60.0
+    z[2010:2020] = -60.0
+    d = to_dev(x)
+    log("layer extreme T=2100")
+    y, o, s = gdn.layer_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"],
+                                d["w"], eps=1e-6)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    assert rel_err(o.cpu().numpy(), o_ref) <= CHUNKED_TOL
+    assert rel_err(s.cpu().numpy(), s_ref) <= CHUNKED_TOL
+    y_ref = oracle.out_norm(o_ref, x["z"], x["w"], 1e-6)
+    bad, worst = y_end_to_end_violations(y.cpu().numpy(), o_ref, x["z"], x["w"][None], 1e-6,
+                                         CHUNKED_TOL, y_ref)
+    assert bad == 0, worst
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-2, 1.0])
+def test_norm_other_eps(eps):
+    """The norm alone with other epsilons (0 on rows that are never all zero, and values
+    large enough to dominate the mean of squares): within 1 fp16 ulp of the oracle."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    x = make_inputs(64, seed=29, with_norm=True)
+    o = (0.1 * np.random.default_rng(29).standard_normal(x["v"].shape)).astype(np.float32)
+    d = {n: torch.from_numpy(a).cuda() for n, a in (("o", o), ("z", x["z"]), ("w", x["w"]))}
+    y = gdn.out_norm(d["o"], d["z"], d["w"], eps=eps)
+    torch.cuda.synchronize()
+    dist = f16_ulp_distance(y.cpu().numpy(), oracle.out_norm(o, x["z"], x["w"], eps))
+    assert dist.max() <= 1
+
+
 @pytest.mark.parametrize("T", [5, 32, 55, 56, 100])
 def test_auto_dispatch(T):
     """gdn_recurrence gives the sequential kernel's bits below 56 tokens and the chunked
