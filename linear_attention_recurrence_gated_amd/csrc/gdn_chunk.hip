@@ -304,22 +304,62 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     const float* kf = reinterpret_cast<const float*>(sm.k[RB]);
     const float* vf = reinterpret_cast<const float*>(sm.v[RB]);
 
-    // (a) This chunk's operands (published by the previous barrier; the buffer is reloaded
-    //     after this chunk's barrier, so everything is read before it).
+    // (a)+(b) This chunk's operands (published by the previous barrier; the buffer is
+    //     reloaded after this chunk's barrier, so everything is read before it) and the
+    //     partial K S0 over this wave's 64 rows (the state registers are the B operand as
+    //     they are).  The reads go out in the order the products consume them: all K tiles
+    //     and the first Q tiles before the first product, the rest in batches behind the
+    //     products of each row tile, so that every batch lands while the matrix core is
+    //     busy instead of all of them queueing on the LDS at once after the barrier.  The
+    //     fences keep the compiler from merging the batches back into one.
     f32x4 ka[4][2], qa[4][2];
     float kt[4][2][4];
+    f32x4 T00, T10, T11, Pa, Pb, eg[2], eb[2], vv[2];
+    float egl;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        ka[rt][tt] = sm.k[RB][ka_i[rt] + 16 * 32 * tt];
-        qa[rt][tt] = sm.q[RB][ka_i[rt] + 16 * 32 * tt];
+      for (int tt = 0; tt < 2; ++tt) ka[rt][tt] = sm.k[RB][ka_i[rt] + 16 * 32 * tt];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) qa[0][tt] = sm.q[RB][ka_i[0] + 16 * 32 * tt];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 Wp[2], Qp[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) Wp[i] = Qp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto w_rt = [&](int rt) {  // row tile rt's share of the partial K S0
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) Wp[tt] = mfma16x16x4(ka[rt][tt][r], S[rt][r], Wp[tt]);
+    };
+    auto kt_rt = [&](int rt) {  // K^T operands of row tile rt for the state update
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) kt[rt][tt][r] = kf[kt_i[rt][r] + 16 * 32 * 4 * tt];
-      }
-    const f32x4 T00 = sm.T[RB][t00_i], T10 = sm.T[RB][t10_i], T11 = sm.T[RB][t11_i];
-    const f32x4 Pa = sm.P[RB][pa_i], Pb = sm.P[RB][pb_i];
-    f32x4 eg[2], eb[2], vv[2];
+    };
+    w_rt(0);
+#pragma unroll
+    for (int rt = 1; rt < 3; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) qa[rt][tt] = sm.q[RB][ka_i[rt] + 16 * 32 * tt];
+    __builtin_amdgcn_sched_barrier(0);
+    w_rt(1);
+    kt_rt(0);
+    kt_rt(1);
+    __builtin_amdgcn_sched_barrier(0);
+    w_rt(2);
+    kt_rt(2);
+    kt_rt(3);
+    __builtin_amdgcn_sched_barrier(0);
+    w_rt(3);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) qa[3][tt] = sm.q[RB][ka_i[3] + 16 * 32 * tt];
+    T00 = sm.T[RB][t00_i];
+    T10 = sm.T[RB][t10_i];
+    T11 = sm.T[RB][t11_i];
+    Pa = sm.P[RB][pa_i];
+    Pb = sm.P[RB][pb_i];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       eg[tt] = sm.misc[RB][4 * tt + q4];
@@ -327,20 +367,11 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) vv[tt][r] = vf[vv_i + 32 * r + 16 * 32 * tt];
     }
-    const float egl = reinterpret_cast<const float*>(sm.misc[RB])[64];
+    egl = reinterpret_cast<const float*>(sm.misc[RB])[64];
+    __builtin_amdgcn_sched_barrier(0);
 
-    // (b) Partial K S0 over this wave's 64 rows (the state registers are the B operand as
-    //     they are), then partial Q S0, whose products cover the exchange: a few before
-    //     the partial K S0 is written, the rest after the barrier while it is read back.
-    f32x4 Wp[2], Qp[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) Wp[i] = Qp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) Wp[tt] = mfma16x16x4(ka[rt][tt][r], S[rt][r], Wp[tt]);
+    //     Then the partial Q S0, whose products cover the exchange: a few before the
+    //     partial K S0 is written, the rest after the barrier while it is read back.
     auto qs = [&](int rt, int r) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) Qp[tt] = mfma16x16x4(qa[rt][tt][r], S[rt][r], Qp[tt]);
