@@ -308,10 +308,11 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     //     reloaded after this chunk's barrier, so everything is read before it) and the
     //     partial K S0 over this wave's 64 rows (the state registers are the B operand as
     //     they are).  The reads go out in the order the products consume them: all K tiles
-    //     and the first Q tiles before the first product, the rest in batches behind the
-    //     products of each row tile, so that every batch lands while the matrix core is
-    //     busy instead of all of them queueing on the LDS at once after the barrier.  The
-    //     fences keep the compiler from merging the batches back into one.
+    //     and the first Q tiles before the first product, the rest in three batches behind
+    //     the products of the first three row tiles (the other Q tiles with the first K^T
+    //     tile, then the operators, then the last K^T tiles), so that every batch lands
+    //     while the matrix core is busy instead of all of them queueing on the LDS at once
+    //     after the barrier.  The fences keep the compiler from merging the batches.
     f32x4 ka[4][2], qa[4][2];
     float kt[4][2][4];
     f32x4 T00, T10, T11, Pa, Pb, eg[2], eb[2], vv[2];
@@ -340,26 +341,24 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     };
     w_rt(0);
 #pragma unroll
-    for (int rt = 1; rt < 3; ++rt)
+    for (int rt = 1; rt < 4; ++rt)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) qa[rt][tt] = sm.q[RB][ka_i[rt] + 16 * 32 * tt];
+    kt_rt(0);
     __builtin_amdgcn_sched_barrier(0);
     w_rt(1);
-    kt_rt(0);
     kt_rt(1);
+    T00 = sm.T[RB][t00_i];
+    T10 = sm.T[RB][t10_i];
+    T11 = sm.T[RB][t11_i];
+    Pa = sm.P[RB][pa_i];
+    Pb = sm.P[RB][pb_i];
     __builtin_amdgcn_sched_barrier(0);
     w_rt(2);
     kt_rt(2);
     kt_rt(3);
     __builtin_amdgcn_sched_barrier(0);
     w_rt(3);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) qa[3][tt] = sm.q[RB][ka_i[3] + 16 * 32 * tt];
-    T00 = sm.T[RB][t00_i];
-    T10 = sm.T[RB][t10_i];
-    T11 = sm.T[RB][t11_i];
-    Pa = sm.P[RB][pa_i];
-    Pb = sm.P[RB][pb_i];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       eg[tt] = sm.misc[RB][4 * tt + q4];
