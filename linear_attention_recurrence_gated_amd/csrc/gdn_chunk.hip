@@ -74,35 +74,68 @@ __device__ __forceinline__ void prep_item(const ChunkArgs& a, int c, int kh, Pre
   __syncthreads();
 
   // 2. Gram tiles on the matrix cores.  Needed: the lower-triangular 16x16 tiles
-  //    (0,0), (1,0), (1,1) of K K^T and of Q K^T; wave w takes tiles w and w + 4.  The
-  //    operands come straight from global memory into registers (lane: row l % 16, four
-  //    keys 4 (l / 16) of each group of 16): the K and Q rows of the chunk, through
-  //    descriptors whose range ends with the call's last token, so rows past it read as 0.
+  //    (0,0), (1,0), (1,1) of K K^T and of Q K^T.  The waves split the keys: wave w forms
+  //    all six tiles over keys 32 w .. 32 w + 31, from the K and Q rows of the chunk loaded
+  //    once, straight from global memory into registers (lane: row l % 16, four keys
+  //    4 (l / 16) of each group of 16), through descriptors whose range ends with the
+  //    call's last token, so rows past it read as 0.  One round trip to memory per wave;
+  //    the four partial tiles are then added in a fixed order, (w0 + w2) + (w1 + w3),
+  //    through sm.A, which step 3 only fills afterwards.
   const int nv = min(kChunk, a.n_tok - c0);  // tokens of the chunk (>= 1)
   const size_t row0 = ((size_t)(a.t_begin + c0) * Hk + kh) * kDim;
   const uint32_t rbytes = (uint32_t)(((nv - 1) * Hk + 1) * kDim * 4);
   const buf_rsrc rk = make_rsrc(a.k + row0, rbytes), rq = make_rsrc(a.q + row0, rbytes);
-  for (int tile = __builtin_amdgcn_readfirstlane(w); tile < 6; tile += 4) {  // (uniform)
-    const int mat = tile / 3, sub = tile % 3;
-    const int ti = sub == 0 ? 0 : 1, tj = sub == 2 ? 1 : 0;
-    const uint32_t lane_col = 16 * (l >> 4);  // bytes
-    const uint32_t offa = (uint32_t)((16 * ti + (l & 15)) * Hk * kDim * 4) + lane_col;
-    const uint32_t offb = (uint32_t)((16 * tj + (l & 15)) * Hk * kDim * 4) + lane_col;
-    const buf_rsrc ra = mat == 0 ? rk : rq;
-    f32x4 av[kDim / 16], bv[kDim / 16];
+  {
+    f32x4 kr[2][2], qr[2][2];  // [row tile][group of 16 keys]
 #pragma unroll
-    for (int s = 0; s < kDim / 16; ++s) {
-      av[s] = buf_load4(ra, offa + 64 * s);
-      bv[s] = buf_load4(rk, offb + 64 * s);
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        const uint32_t off = (uint32_t)((16 * ti + (l & 15)) * Hk * kDim * 4) +
+                             16 * (l >> 4) + 64 * (2 * w + sg);
+        kr[ti][sg] = buf_load4(rk, off);
+        qr[ti][sg] = buf_load4(rq, off);
+      }
+    f32x4 acc[6];  // K K^T (0,0), (1,0), (1,1), then Q K^T (0,0), (1,0), (1,1)
+#pragma unroll
+    for (int t = 0; t < 6; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[0] = mfma16x16x4(kr[0][sg][r], kr[0][sg][r], acc[0]);
+        acc[1] = mfma16x16x4(kr[1][sg][r], kr[0][sg][r], acc[1]);
+        acc[2] = mfma16x16x4(kr[1][sg][r], kr[1][sg][r], acc[2]);
+        acc[3] = mfma16x16x4(qr[0][sg][r], kr[0][sg][r], acc[3]);
+        acc[4] = mfma16x16x4(qr[1][sg][r], kr[0][sg][r], acc[4]);
+        acc[5] = mfma16x16x4(qr[1][sg][r], kr[1][sg][r], acc[5]);
+      }
+    f32x4* const part = reinterpret_cast<f32x4*>(&sm.A[0][0][0]);  // [2][6][64]
+    if (w >= 2) {
+#pragma unroll
+      for (int t = 0; t < 6; ++t) part[((w - 2) * 6 + t) * 64 + l] = acc[t];
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    if (w < 2) {
 #pragma unroll
-    for (int s = 0; s < kDim / 16; ++s)
+      for (int t = 0; t < 6; ++t) acc[t] += part[(w * 6 + t) * 64 + l];
+      if (w == 1) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc = mfma16x16x4(av[s][r], bv[s][r], acc);
+        for (int t = 0; t < 6; ++t) part[(6 + t) * 64 + l] = acc[t];
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      sm.gram[mat][16 * ti + 4 * (l >> 4) + r][16 * tj + (l & 15)] = acc[r];
+      for (int t = 0; t < 6; ++t) {
+        const f32x4 sum = acc[t] + part[(6 + t) * 64 + l];
+        const int mat = t / 3, sub = t % 3;
+        const int ti = sub == 0 ? 0 : 1, tj = sub == 2 ? 1 : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sm.gram[mat][16 * ti + 4 * (l >> 4) + r][16 * tj + (l & 15)] = sum[r];
+      }
+    }
   }
   __syncthreads();
 
