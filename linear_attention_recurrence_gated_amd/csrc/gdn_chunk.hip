@@ -341,11 +341,12 @@ __device__ __forceinline__ void scan_wave(const ChunkArgs& a, int h, int kh, int
     //     reloaded after this chunk's barrier, so everything is read before it) and the
     //     partial K S0 over this wave's 64 rows (the state registers are the B operand as
     //     they are).  The reads go out in the order the products consume them: all K tiles
-    //     and the first Q tiles before the first product, the rest in three batches behind
-    //     the products of the first three row tiles (the other Q tiles with the first K^T
-    //     tile, then the operators, then the last K^T tiles), so that every batch lands
-    //     while the matrix core is busy instead of all of them queueing on the LDS at once
-    //     after the barrier.  The fences keep the compiler from merging the batches.
+    //     and the first Q tiles before the first product, the rest in four batches, one
+    //     behind the products of each row tile (the other Q tiles with the first K^T tile,
+    //     the second K^T tile with the operators T and P, the last two K^T tiles, the
+    //     decays and V), so that every batch lands while the matrix core is busy instead
+    //     of all of them queueing on the LDS at once after the barrier.  The fences keep
+    //     the compiler from merging the batches.
     f32x4 ka[4][2], qa[4][2];
     float kt[4][2][4];
     f32x4 T00, T10, T11, Pa, Pb, eg[2], eb[2], vv[2];
