@@ -122,20 +122,69 @@ def calibration_copy():
     torch.cuda.synchronize()
 
 
-def cpu_baseline(x, tokens):
-    """The FP64 oracle (recurrence + norm) on the first `tokens` tokens, all 48 heads."""
+def _oracle_time(x, threads, norm):
+    """Seconds of one FP64 oracle pass (recurrence, plus the norm if `norm`) over the
+    arrays of `x` with an explicit OpenMP thread count (the oracle keeps the last count it
+    was given, so every call passes its own)."""
     import oracle
-    sl = {n: (a[:tokens] if n in ("q", "k", "v", "g", "beta", "z") else a) for n, a in x.items()}
-    threads = oracle.max_threads()
     t0 = time.perf_counter()
-    o, _ = oracle.recurrence(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["s0"],
+    o, _ = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"],
                              threads=threads)
-    oracle.out_norm(o, sl["z"], sl["w"], 1e-6, threads=threads)
-    dt = time.perf_counter() - t0
+    if norm:
+        oracle.out_norm(o, x["z"], x["w"], 1e-6, threads=threads)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(x, tokens, threads):
+    """The FP64 oracle (recurrence + norm) on the first `tokens` tokens, all 48 heads."""
+    sl = {n: (a[:tokens] if n in ("q", "k", "v", "g", "beta", "z") else a) for n, a in x.items()}
+    dt = _oracle_time(sl, threads, True)
     return {"value": dt * 1e6 / tokens, "unit": "µs/token/layer", "cores": threads,
             "kind": "oracle",
             "sample": "first %d of the 32768 tokens, all 48 value heads: FP64 recurrence + "
                       "gated RMS norm (%.1f s wall)" % (tokens, dt)}
+
+
+def cpu_oracle_configs(threads, gpu):
+    """The FP64 oracle timed on the other workloads of the family, for context: the
+    recurrence at T = 64 and over the edge-length sweep (1 thread and all threads), one
+    layer of 8192 tokens with the norm (1 thread and all threads), and the 36-layer stack of
+    2048-token layers with the norm (all threads).  Compute only (input generation is
+    outside the clock).  `gpu` maps a workload to the GPU's µs/token/layer, for the ratio."""
+    from linear_attention_recurrence_gated_amd import EDGE_LENGTHS, make_inputs
+
+    def entry(tokens, secs, gpu_us=None):
+        e = {"us_per_token_layer": round(secs * 1e6 / tokens, 3),
+             "gflops_f": round(FLOP_PER_TOKEN * tokens / secs / 1e9, 3), "seconds": round(secs, 3)}
+        if gpu_us:
+            e["oracle_over_gpu"] = round(secs * 1e6 / tokens / gpu_us, 1)
+        return e
+
+    out = {"cores_all": threads}
+    x = make_inputs(64, seed=0)
+    out["T64_recurrence"] = {"threads_1": entry(64, _oracle_time(x, 1, False)),
+                             "threads_all": entry(64, _oracle_time(x, threads, False))}
+    xs = [make_inputs(T, seed=0) for T in EDGE_LENGTHS]
+    n = sum(EDGE_LENGTHS)
+    out["edge_lengths_recurrence"] = {
+        "tokens": n,
+        "threads_1": entry(n, sum(_oracle_time(xe, 1, False) for xe in xs)),
+        "threads_all": entry(n, sum(_oracle_time(xe, threads, False) for xe in xs))}
+    del xs
+    print("bench: CPU oracle, T=8192 layer", file=sys.stderr, flush=True)
+    x = make_inputs(8192, seed=0, with_norm=True)
+    g8 = gpu.get("seq_layer_T8192_us_per_token")
+    out["T8192_recurrence_norm"] = {"threads_1": entry(8192, _oracle_time(x, 1, True), g8),
+                                    "threads_all": entry(8192, _oracle_time(x, threads, True), g8)}
+    del x
+    print("bench: CPU oracle, 36-layer stack", file=sys.stderr, flush=True)
+    secs = 0.0
+    for layer in range(36):
+        x = make_inputs(2048, seed=layer, with_norm=True)
+        secs += _oracle_time(x, threads, True)
+    out["stack36_T2048_recurrence_norm"] = {
+        "threads_all": entry(36 * 2048, secs, gpu.get("stack36_T2048_us_per_token_layer"))}
+    return out
 
 
 def _median(xs):
@@ -324,12 +373,17 @@ def main():
     if args.calibration_copy:
         calibration_copy()
 
-    cpu = None
+    cpu = cpu_cfg = None
     if args.cpu_tokens > 0:
-        print("bench: CPU oracle on %d tokens" % args.cpu_tokens, file=sys.stderr, flush=True)
-        cpu = cpu_baseline(x, min(args.cpu_tokens, T))
+        import oracle
+        threads = oracle.max_threads()  # before any call sets its own count
+        print("bench: CPU oracle on %d tokens, %d threads" % (args.cpu_tokens, threads),
+              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x, min(args.cpu_tokens, T), threads)
+        cpu_cfg = cpu_oracle_configs(threads, ctx)
 
     traffic = traffic_from_profile()
+    launch_s = scan_avg_ms * 1e-3
     line = {
         "metric": METRIC,
         "value": round(ms_per_step * 1e3 / T, 6),
@@ -358,6 +412,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
             "traffic": traffic,
+            "hbm_GBps": round(traffic / launch_s / 1e9, 1) if traffic else None,
+            "hbm_frac": round(traffic / launch_s / 1e9 / PEAK_HBM_GBS, 4) if traffic else None,
             "flop_per_launch": flop_per_launch,
             "avg_launch_ms": round(scan_avg_ms, 5),
             "launches_timed": len(scan_full_ms),
@@ -376,6 +432,7 @@ def main():
             "outputs_finite": y_ok,
         },
         "cpu_baseline": cpu,
+        "cpu_oracle_other_workloads": cpu_cfg,
     }
     print(json.dumps(line), flush=True)
 

@@ -25,7 +25,9 @@
  *    the library prints nothing.
  *  - Only dk = dv = 128 is supported; n_v_heads must be a positive multiple of
  *    n_k_heads with at most 4 value heads per key head; T * n_v_heads * dv must be
- *    below 2^31 (32-bit element offsets).
+ *    below 2^31 (32-bit element offsets) and, for the recurrence and layer calls,
+ *    2048 * n_v_heads * dv * 4 below 2^31 (32-bit byte counts over one 2048-token
+ *    super-block: n_v_heads <= 2047).
  *    Anything else is GDN_ERR_BAD_SHAPE -- there is no fallback path.
  *  - Layouts (row-major, contiguous, float32 unless stated):
  *        q, k         [T][n_k_heads][dk]   (the library applies no normalisation/scale)
@@ -49,8 +51,8 @@ enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                                  */
   GDN_ERR_BAD_SHAPE = 2,    /* T < 0, dk/dv != 128, heads < 1, n_v_heads % n_k_heads != 0,
-                               n_v_heads / n_k_heads > 4, T * n_v_heads * dv >= 2^31, or
-                               a negative / non-finite eps                                 */
+                               n_v_heads / n_k_heads > 4, T * n_v_heads * dv >= 2^31,
+                               n_v_heads > 2047, or a negative / non-finite eps             */
   GDN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned                            */
   GDN_ERR_ALIASING = 4,     /* an output overlaps an input or another output
                                (state_out == state_in exactly is allowed)                  */

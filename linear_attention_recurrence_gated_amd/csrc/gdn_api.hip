@@ -4,8 +4,39 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 #include "gdn_kernels.h"
+
+namespace gdn {
+
+// Compute units per device, filled on first use (0 = not yet queried).  Racing first calls
+// store the same value, so relaxed atomics suffice.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cu_count[kMaxDevices];
+
+hipError_t device_cu_count(hipStream_t stream, int* cus) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cus = cached;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return hipSuccess;
+}
+
+}  // namespace gdn
 
 namespace {
 
@@ -36,7 +67,12 @@ int check_shape(int64_t T, int n_k_heads, int n_v_heads, int dk, int dv) {
   if (dk != gdn::kDim || dv != gdn::kDim) return GDN_ERR_BAD_SHAPE;
   if (n_v_heads % n_k_heads != 0) return GDN_ERR_BAD_SHAPE;
   if (n_v_heads / n_k_heads > gdn::kMaxGroup) return GDN_ERR_BAD_SHAPE;
+  // 32-bit element offsets over a whole call ...
   if (T * (int64_t)n_v_heads * dv >= ((int64_t)1 << 31)) return GDN_ERR_BAD_SHAPE;
+  // ... and 32-bit byte counts over one super-block (the chunked kernels' buffer ranges of
+  // the o, v and y rows of a 2048-token super-block; n_k_heads <= n_v_heads)
+  if ((int64_t)gdn::kSuperBlock * n_v_heads * dv * (int64_t)sizeof(float) >= ((int64_t)1 << 31))
+    return GDN_ERR_BAD_SHAPE;
   return GDN_OK;
 }
 

@@ -767,7 +767,9 @@ hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_
   // the prep workgroups fill the CUs the scan leaves free (at least 32 of them)
   int n_prep = 0;
   if (prep_next) {
-    n_prep = kNumCUs - f.n_scan;
+    int cus = 0;
+    if (const hipError_t e = device_cu_count(stream, &cus)) return e;
+    n_prep = cus - f.n_scan;
     if (n_prep < 32) n_prep = 32;
   }
   void* args[] = {&f};

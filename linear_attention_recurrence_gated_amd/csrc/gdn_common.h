@@ -106,11 +106,15 @@ __device__ __forceinline__ void buf_store2(buf_rsrc r, uint32_t byte_off, u32x2 
 // Direct global -> LDS load (gfx950): lane l's 16 bytes at byte_off (from the descriptor's
 // base, checked against its size: out of range reads as 0) land at LDS address
 // lds_base + LDS_OFF + 16 l, without passing through registers.  The wave-uniform LDS
-// address travels in m0, which nothing else in these kernels uses.  Issued as inline
-// assembly so that the compiler does not treat it as a pending LDS write (it would then
-// wait for every such load before the next LDS read); the caller waits with wait_vm_lgkm0
-// before the barrier that publishes the data.  LDS_OFF is an immediate, so an unrolled run
-// of loads keeps one base register rather than one per destination.
+// address travels in m0.  Issued as inline assembly so that the compiler does not treat it
+// as a pending LDS write (it would then wait for every such load before the next LDS
+// read); the caller waits with wait_vm_lgkm0 before the barrier that publishes the data.
+// On this GFX9-family target a scalar-ALU write of m0 needs one wait state before an
+// LDS-DMA load reads it (the compiler's own lowering of these loads puts an s_nop 0 there,
+// and its hazard recogniser does not look inside inline assembly), so the sequence carries
+// that s_nop itself; m0 is declared clobbered so the compiler keeps nothing of its own in
+// it across the load.  LDS_OFF is an immediate, so an unrolled run of loads keeps one base
+// register rather than one per destination.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char* lds_cptr;
 __device__ __forceinline__ i32x4 make_desc(const void* base, int bytes) {
@@ -122,8 +126,8 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 template <int LDS_OFF>
 __device__ __forceinline__ void dma16(const i32x4& desc, uint32_t byte_off, uint32_t lds_base) {
-  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
-               :: "s"(lds_base), "i"(LDS_OFF), "v"(byte_off), "s"(desc) : "scc");
+  asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               :: "s"(lds_base), "i"(LDS_OFF), "v"(byte_off), "s"(desc) : "scc", "m0");
 }
 // Loads I = 0, 1, ... of a run: destination LDS_OFF + 1024 I, per-lane offsets off[I].
 template <int LDS_OFF, int... I>

@@ -9,7 +9,6 @@
 namespace gdn {
 
 constexpr int kDim = 128;          // dk = dv supported by every kernel
-constexpr int kNumCUs = 256;       // compute units of an MI355X
 constexpr int kMaxGroup = 4;       // value heads per key head supported
 constexpr int kChunk = 32;         // tokens per WY chunk
 constexpr int kSuperBlock = 2048;  // tokens whose chunk operators are prepared at once
@@ -62,6 +61,9 @@ struct NormArgs {
   int n_rows;  // T * n_v_heads
   int n_v_heads;
 };
+
+// Compute units of the device that `stream` runs on (queried once per device, then cached).
+hipError_t device_cu_count(hipStream_t stream, int* cus);
 
 hipError_t launch_seq(const SeqArgs& a, int group, hipStream_t stream);
 hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);

@@ -95,10 +95,42 @@ def _shapes(q, v):
     return T, Hk, Hv, dk, dv
 
 
+def check_shapes(q, k, v, g, beta, state_in, state_out=None, o=None, z=None, w=None, y=None):
+    """Check every operand's shape against (T, n_k_heads, dk) from q and (n_v_heads, dv)
+    from v; raise ValueError on the first mismatch.  Only ``.shape`` is read, so this runs
+    on any array (the library receives bare pointers and sizes: a short operand would
+    otherwise be read or written past its end).  Returns (T, Hk, Hv, dk, dv)."""
+    if len(q.shape) != 3 or len(v.shape) != 3:
+        raise ValueError("q must be [T][n_k_heads][dk] and v [T][n_v_heads][dv]; got q %s, v %s"
+                         % (tuple(q.shape), tuple(v.shape)))
+    T, Hk, Hv, dk, dv = _shapes(q, v)
+    want = {"k": (k, (T, Hk, dk)), "v": (v, (T, Hv, dv)), "g": (g, (T, Hv)),
+            "beta": (beta, (T, Hv)), "state_in": (state_in, (Hv, dk, dv)),
+            "state_out": (state_out, (Hv, dk, dv)), "o": (o, (T, Hv, dv)),
+            "z": (z, (T, Hv, dv)), "w": (w, (Hv, dv)), "y": (y, (T, Hv, dv))}
+    for name, (t, shape) in want.items():
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s (T=%d, n_k_heads=%d, n_v_heads=%d, "
+                             "dk=%d, dv=%d)" % (name, tuple(t.shape), shape, T, Hk, Hv, dk, dv))
+    return T, Hk, Hv, dk, dv
+
+
+def check_norm_shapes(o, z, w, y=None):
+    """Shapes of the output norm's operands: o, z, y [T][n_v_heads][dv], w [n_v_heads][dv]."""
+    if len(o.shape) != 3:
+        raise ValueError("o must be [T][n_v_heads][dv]; got %s" % (tuple(o.shape),))
+    T, Hv, dv = o.shape
+    for name, t, shape in (("z", z, (T, Hv, dv)), ("w", w, (Hv, dv)), ("y", y, (T, Hv, dv))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+    return T, Hv, dv
+
+
 def recurrence_seq(q, k, v, g, beta, state_in, state_out=None, o=None, stream=None):
     """Sequential kernel.  Returns (o, state_out); state_out may be state_in (in place)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in")):
         _f32(t, n)
+    check_shapes(q, k, v, g, beta, state_in, state_out, o)
     T, Hk, Hv, dk, dv = _shapes(q, v)
     if state_out is None:
         state_out = torch.empty_like(state_in)
@@ -147,6 +179,7 @@ def recurrence_chunked(q, k, v, g, beta, state_in, state_out=None, o=None, ws=No
     super-block's scan kernel."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in")):
         _f32(t, n)
+    check_shapes(q, k, v, g, beta, state_in, state_out, o)
     T, Hk, Hv, dk, dv = _shapes(q, v)
     if state_out is None:
         state_out = torch.empty_like(state_in)
@@ -176,6 +209,7 @@ def recurrence(q, k, v, g, beta, state_in, state_out=None, o=None, ws=None, stre
     chunked from there).  Returns (o, state_out)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in")):
         _f32(t, n)
+    check_shapes(q, k, v, g, beta, state_in, state_out, o)
     T, Hk, Hv, dk, dv = _shapes(q, v)
     if state_out is None:
         state_out = torch.empty_like(state_in)
@@ -200,6 +234,7 @@ def layer_chunked(q, k, v, g, beta, state_in, z, w, eps=1e-6, state_out=None, o=
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in"),
                  (z, "z"), (w, "w")):
         _f32(t, n)
+    check_shapes(q, k, v, g, beta, state_in, state_out, o, z, w, y)
     T, Hk, Hv, dk, dv = _shapes(q, v)
     if state_out is None:
         state_out = torch.empty_like(state_in)
@@ -228,7 +263,7 @@ def layer_chunked(q, k, v, g, beta, state_in, z, w, eps=1e-6, state_out=None, o=
 def out_norm(o, z, w, eps=1e-6, y=None, stream=None):
     """Gated RMS output norm.  Returns y as a float16 tensor [T][Hv][dv]."""
     _f32(o, "o"); _f32(z, "z"); _f32(w, "w")
-    T, Hv, dv = o.shape
+    T, Hv, dv = check_norm_shapes(o, z, w, y)
     if y is None:
         y = torch.empty(o.shape, dtype=torch.float16, device=o.device)
     if y.dtype != torch.float16 or not y.is_contiguous() or not y.is_cuda:

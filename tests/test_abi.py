@@ -105,6 +105,8 @@ def test_recurrence_validation(L, fn):
     assert fn(L, a, Hv=40) == SHAPE
     assert fn(L, a, Hk=8, Hv=48) == SHAPE                       # 6 value heads per key head
     assert fn(L, a, T=(1 << 31) // (48 * 128) + 1) == SHAPE     # 32-bit element offsets
+    # 32-bit byte counts over one 2048-token super-block: 2048 * Hv * 128 * 4 < 2^31
+    assert fn(L, a, T=2, Hk=2048, Hv=2048) == SHAPE
     assert fn(L, dict(a, v=a["v"] + 4)) == MISAL
     assert fn(L, dict(a, o=a["q"])) == ALIAS                    # output over an input
     assert fn(L, dict(a, s_out=a["v"])) == ALIAS
@@ -112,6 +114,19 @@ def test_recurrence_validation(L, fn):
     assert fn(L, dict(a, o=a["s_out"])) == ALIAS
     # T = 0 in place: nothing to do, no device call
     assert fn(L, dict(a, s_out=a["s_in"]), T=0) == OK
+
+
+def test_super_block_byte_count_limit(L):
+    """The largest head count whose 2048-token super-block keeps every byte count below
+    2^31 is accepted by validation (T = 0 in place: no device call), the next is not."""
+    a = _addrs()
+    ok = dict(a, s_out=a["s_in"])
+    assert _seq(L, ok, T=0, Hk=2047, Hv=2047) == OK
+    assert _chunked(L, ok, T=0, Hk=2047, Hv=2047) == OK
+    assert _seq(L, ok, T=0, Hk=2048, Hv=2048) == SHAPE
+    assert _chunked(L, ok, T=0, Hk=2048, Hv=2048) == SHAPE
+    assert L.gdn_chunked_workspace_bytes(2048, 2048, 128, 128) == 0
+    assert L.gdn_chunked_workspace_bytes(2047, 2047, 128, 128) > 0
 
 
 def test_seq_dims(L):

@@ -3,10 +3,11 @@
 Every HIP source is compiled to assembly with the library's own flags, and the listing is
 checked for rules the design relies on:
 
-* m0 is written only by the direct global-to-LDS load sequences (`s_add_u32 m0, ...`
-  immediately before each `buffer_load_dwordx4 ... lds`): those loads take their LDS
-  address from m0 without declaring it, which is safe only while nothing else in the
-  kernels uses the register;
+* m0 is written only by the direct global-to-LDS load sequences (`s_add_u32 m0, ...`,
+  then one `s_nop 0`, then `buffer_load_dwordx4 ... lds`): on this GFX9-family target a
+  scalar-ALU write of m0 needs one wait state before an LDS-DMA load reads it, and the
+  compiler's hazard recogniser cannot see inside the inline assembly that issues them, so
+  the sequence must carry the wait itself;
 * no packed FP32 vector instruction (`v_pk_add_f32`, `v_pk_mul_f32`, `v_pk_fma_f32`)
   appears: the build disables them;
 * no scalar memory store or scalar atomic appears: every store goes through the vector
@@ -68,10 +69,26 @@ def test_m0_only_addressed_by_direct_loads(listings):
         for i, (fn, op, line) in enumerate(ins):
             if re.search(r"\bm0\b", line):
                 assert op == "s_add_u32" and line.split()[1] == "m0,", (name, fn, line)
-                nxt = ins[i + 1][2]
+                # one wait state between the scalar write of m0 and the load that reads it
+                assert ins[i + 1][1] == "s_nop" and ins[i + 1][2].split()[1] == "0", \
+                    (name, line, ins[i + 1][2])
+                nxt = ins[i + 2][2]
                 assert nxt.startswith("buffer_load_dwordx4") and nxt.endswith(" lds"), (name, line, nxt)
                 seen += 1
     assert seen > 0  # the direct loads are there
+
+
+def test_every_direct_load_follows_its_m0_write_with_a_wait_state(listings):
+    """Each LDS-DMA load is preceded by `s_nop 0` and, before that, the m0 write."""
+    seen = 0
+    for name, ins in listings.items():
+        for i, (fn, op, line) in enumerate(ins):
+            if op.startswith("buffer_load") and line.endswith(" lds"):
+                assert ins[i - 1][1] == "s_nop", (name, fn, ins[i - 1][2], line)
+                assert ins[i - 2][1] == "s_add_u32" and ins[i - 2][2].split()[1] == "m0,", \
+                    (name, fn, ins[i - 2][2], line)
+                seen += 1
+    assert seen > 0
 
 
 def test_no_packed_fp32_vector_instructions(listings):
