@@ -204,6 +204,32 @@ int gdn_layer_chunked_timed(const float* q, const float* k, const float* v, cons
                             void* workspace, size_t workspace_bytes,
                             void* const* scan_events, int n_scan_events, void* stream);
 
+/*
+ * gdn_layer_chunked for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same validation, the
+ * same kernels and the same results bit for bit as gdn_layer_chunked, but without a
+ * workspace argument: the chunked kernels' scratch is a file-scope device array of the
+ * library, 68 MiB per device, which each device holds from the first call on it until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine); the caller still passes every input and output.
+ *
+ *   n_v_heads        : at most 64 (the array holds the operators of two 2048-token
+ *                      super-blocks of 64 value heads); more is GDN_ERR_WORKSPACE.
+ *   first call       : on a device, resolves the array's device address (with that
+ *                      device current); make it outside any graph capture.
+ *   concurrency      : every call on a device uses that device's one array, which keeps
+ *                      the last call's contents (no call depends on them).  Calls on one
+ *                      stream are ordered; calls that overlap on one device (different
+ *                      streams, or several host threads' streams) race on the array and
+ *                      give undefined results.
+ *   Everything else  : as for gdn_layer_chunked.
+ */
+int gdn_layer_chunked_noalloc(const float* q, const float* k, const float* v, const float* g,
+                              const float* beta, const float* state_in, float* state_out,
+                              float* o, const float* z, const float* w, float eps, uint16_t* y,
+                              int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                              void* stream);
+
 /* A static, never-NULL description of a gdn_status value. */
 const char* gdn_status_string(int status);
 

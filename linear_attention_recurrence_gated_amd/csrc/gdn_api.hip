@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "gdn.h"
 #include "gdn_kernels.h"
@@ -33,6 +34,52 @@ hipError_t device_cu_count(hipStream_t stream, int* cus) {
   if (n < 1) return hipErrorInvalidDevice;
   if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
   *cus = n;
+  return hipSuccess;
+}
+
+// Workspace of gdn_layer_chunked_noalloc: a file-scope device array, one copy per device,
+// held from the first call on that device until the process ends.  It holds the chunked
+// kernels' operators for up to kStaticMaxVHeads value heads (both halves of the
+// double-buffered super-block workspace: 2 x 64 chunks x 64 heads x 8704 bytes = 68 MiB).
+// In host code `scratch` names a host-side stand-in, never device memory: every use goes
+// through the address hipGetSymbolAddress returns for the device.
+constexpr int kStaticMaxVHeads = 64;
+constexpr size_t kStaticScratchBytes =
+    2 * (size_t)kChunksPerSB * kStaticMaxVHeads * kSlot * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the device that `stream` runs on, resolved once per
+// device with that device current.
+hipError_t static_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (void* p = g_scratch_ptr[dev].load(std::memory_order_acquire)) {
+    *out = p;
+    return hipSuccess;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (void* p = g_scratch_ptr[dev].load(std::memory_order_acquire)) {
+    *out = p;
+    return hipSuccess;
+  }
+  int cur = 0;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (cur != dev) {
+    const hipError_t e2 = hipSetDevice(cur);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  *out = p;
   return hipSuccess;
 }
 
@@ -309,6 +356,30 @@ int gdn_layer_chunked_timed(const float* q, const float* k, const float* v, cons
   return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
                       dv, workspace, workspace_bytes, NormOut{z, w, eps, y}, scan_events,
                       n_scan_events, stream);
+}
+
+int gdn_layer_chunked_noalloc(const float* q, const float* k, const float* v, const float* g,
+                              const float* beta, const float* state_in, float* state_out,
+                              float* o, const float* z, const float* w, float eps, uint16_t* y,
+                              int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                              void* stream) {
+  // Every argument is validated before the first HIP call (the workspace is the library's
+  // own array, so it takes part in no caller-side check).
+  if (int st = check_shape(T, n_k_heads, n_v_heads, dk, dv)) return st;
+  if (n_v_heads > gdn::kStaticMaxVHeads) return GDN_ERR_WORKSPACE;
+  if (!y || !w || (T > 0 && !z)) return GDN_ERR_NULL_POINTER;
+  if (int st = check_recurrence(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads,
+                                n_v_heads, dk, dv, nullptr, 0, false))
+    return st;
+  if (int st = check_layer_norm(q, k, v, g, beta, state_in, state_out, o, nullptr, 0, z, w, eps,
+                                y, T, n_k_heads, n_v_heads))
+    return st;
+  void* ws = nullptr;
+  if (const hipError_t e = gdn::static_scratch(static_cast<hipStream_t>(stream), &ws))
+    return hip_fail(e);
+  return chunked_impl(q, k, v, g, beta, state_in, state_out, o, T, n_k_heads, n_v_heads, dk,
+                      dv, ws, gdn::kStaticScratchBytes, NormOut{z, w, eps, y}, nullptr, 0,
+                      stream);
 }
 
 int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint16_t* y,

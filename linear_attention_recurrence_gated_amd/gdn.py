@@ -33,6 +33,8 @@ SIGNATURES = {
                                _I, _I, _P, _SZ, _P]),
     "gdn_layer_chunked_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64, _I,
                                      _I, _I, _I, _P, _SZ, _P, _I, _P]),
+    "gdn_layer_chunked_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64,
+                                       _I, _I, _I, _I, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
     "gdn_last_hip_error": (_I, []),
     "gdn_abi_version": (_I, []),
@@ -257,6 +259,28 @@ def layer_chunked(q, k, v, g, beta, state_in, z, w, eps=1e-6, state_out=None, o=
         arr = (ctypes.c_void_p * max(1, len(scan_events)))(*scan_events)
         st = lib().gdn_layer_chunked_timed(*args, arr, len(scan_events), _stream(stream, q.device))
         _check("gdn_layer_chunked_timed", st)
+    return y, o, state_out
+
+
+NOALLOC_MAX_V_HEADS = 64  # the static workspace's head count (gdn.h)
+
+
+def layer_chunked_noalloc(q, k, v, g, beta, state_in, z, w, state_out, o, y, eps=1e-6,
+                          stream=None):
+    """gdn_layer_chunked_noalloc: the one-call layer with the library's static workspace.
+    Every output is the caller's (nothing is allocated here either).  Returns
+    (y, o, state_out)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state_in, "state_in"),
+                 (z, "z"), (w, "w"), (state_out, "state_out"), (o, "o")):
+        _f32(t, n)
+    check_shapes(q, k, v, g, beta, state_in, state_out, o, z, w, y)
+    T, Hk, Hv, dk, dv = _shapes(q, v)
+    if y.dtype != torch.float16 or not y.is_contiguous() or not y.is_cuda:
+        raise TypeError("y must be a contiguous float16 CUDA tensor")
+    st = lib().gdn_layer_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
+        _ptr(z), _ptr(w), float(eps), _ptr(y), T, Hk, Hv, dk, dv, _stream(stream, q.device))
+    _check("gdn_layer_chunked_noalloc", st)
     return y, o, state_out
 
 

@@ -179,6 +179,33 @@ def test_layer_validation(L):
     assert _layer(L, dict(a, s_out=a["s_in"]), T=0) == OK   # nothing to do
 
 
+def _noalloc(L, a, T=64, Hk=16, Hv=48, eps=1e-6):
+    P = ctypes.c_void_p
+    return L.gdn_layer_chunked_noalloc(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]),
+                                       P(a["beta"]), P(a["s_in"]), P(a["s_out"]), P(a["o"]),
+                                       P(a["z"]), P(a["w"]), eps, P(a["y"]), T, Hk, Hv, 128,
+                                       128, None)
+
+
+def test_noalloc_validation(L):
+    """The static-workspace layer validates like gdn_layer_chunked, and rejects head counts
+    beyond its array (64 value heads) before any device call."""
+    a = _addrs(Hk=32, Hv=128)
+    assert _noalloc(L, a, Hk=32, Hv=128) == WS
+    assert _noalloc(L, a, Hk=20, Hv=80) == WS
+    assert _noalloc(L, a, Hk=16, Hv=80) == SHAPE                 # 5 value heads per key head
+    a = _addrs()
+    assert _noalloc(L, dict(a, q=0)) == NULLP
+    assert _noalloc(L, dict(a, y=0)) == NULLP
+    assert _noalloc(L, a, T=-1) == SHAPE
+    assert _noalloc(L, a, Hv=40) == SHAPE
+    assert _noalloc(L, a, eps=-1.0) == SHAPE
+    assert _noalloc(L, dict(a, v=a["v"] + 4)) == MISAL
+    assert _noalloc(L, dict(a, o=a["q"])) == ALIAS
+    assert _noalloc(L, dict(a, y=a["o"] + 256)) == ALIAS
+    assert _noalloc(L, dict(a, o=a["z"])) == ALIAS
+
+
 def _auto(L, a, T=64, Hk=16, Hv=48, ws_bytes=None):
     P = ctypes.c_void_p
     if ws_bytes is None:
