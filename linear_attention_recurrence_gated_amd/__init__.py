@@ -7,9 +7,10 @@ that library (argument marshalling only), ``inputs`` the seeded synthetic-input 
 The binding is imported lazily so that the input generator can be used without the
 library; every compute call fails loudly if the library has not been built.
 """
-from .inputs import DK, DV, EDGE_LENGTHS, N_K_HEADS, N_V_HEADS, make_inputs  # noqa: F401
+from .inputs import (DK, DV, EDGE_LENGTHS, N_K_HEADS, N_V_HEADS, make_inputs,  # noqa: F401
+                     make_pre_inputs)
 
-__all__ = ["make_inputs", "EDGE_LENGTHS", "N_K_HEADS", "N_V_HEADS", "DK", "DV", "gdn"]
+__all__ = ["make_inputs", "make_pre_inputs", "EDGE_LENGTHS", "N_K_HEADS", "N_V_HEADS", "DK", "DV", "gdn"]
 
 
 def __getattr__(name):

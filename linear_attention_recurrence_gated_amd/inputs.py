@@ -58,3 +58,34 @@ def make_inputs(T: int, seed: int = 0, n_k_heads: int = N_K_HEADS,
 
 # The edge-length sweep of the pages' parity test (from a non-zero state).
 EDGE_LENGTHS = (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 257, 1000, 4099)
+
+
+def make_pre_inputs(T: int, seed: int = 0, n_k_heads: int = N_K_HEADS,
+                    n_v_heads: int = N_V_HEADS, dk: int = DK, dv: int = DV,
+                    zero_history: bool = False) -> dict:
+    """Seeded synthetic inputs of the step before the recurrence, in the library layout
+    (float32, contiguous):
+
+        x        [T][C]  ~ N(0, 1)      projection output, C = 2*Hk*dk + Hv*dv channels
+                                        (q of each key head, then k, then v of each value head)
+        conv_w   [C][4]  ~ N(0, 0.5)    4-tap conv weights (standard deviation 0.5)
+        hist     [3][C]  ~ N(0, 1)      conv inputs of the 3 tokens before (zeros if
+                                        ``zero_history``: the start of a prompt)
+        a, b     [T][Hv] ~ N(0, 1)      raw gate and beta inputs
+        A_log    [Hv]    = log(U(1, 16)) gate scale (log)
+        dt_bias  [Hv]    ~ N(0, 0.5)    gate bias
+
+    Draw order within one seed (numpy PCG64): x, conv_w, hist, a, b, A_log, dt_bias.  These
+    are draws of the shape of the model's projections, no model."""
+    rng = np.random.default_rng(seed)
+    C = 2 * n_k_heads * dk + n_v_heads * dv
+    out = {}
+    out["x"] = rng.standard_normal((T, C)).astype(np.float32)
+    out["conv_w"] = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    hist = rng.standard_normal((3, C)).astype(np.float32)
+    out["hist"] = np.zeros_like(hist) if zero_history else hist
+    out["a"] = rng.standard_normal((T, n_v_heads)).astype(np.float32)
+    out["b"] = rng.standard_normal((T, n_v_heads)).astype(np.float32)
+    out["A_log"] = np.log(rng.uniform(1.0, 16.0, n_v_heads)).astype(np.float32)
+    out["dt_bias"] = (0.5 * rng.standard_normal(n_v_heads)).astype(np.float32)
+    return out

@@ -5,9 +5,11 @@ baseline leg of ``bench.py`` may import this package.  The product path (the HIP
 and its Python binding) never imports it, and this package imports nothing from the
 product path.  The two sides meet only through the seeded float32 input arrays.
 
-What it computes (O1 recurrence, O2 output norm) is documented, with citations of the
-pages, in ``gdn_oracle.c``; ``forms.py`` holds two independent re-formulations used only
-to pin O1 (the dense per-token form and the chunked WY form).
+What it computes (O1 recurrence, O2 output norm, O3 the step before the recurrence: the
+4-tap causal conv with its history, the q/k normalisation and the gate/beta formation) is
+documented, with citations of the pages, in ``gdn_oracle.c``; ``forms.py`` holds two
+independent re-formulations used only to pin O1 (the dense per-token form and the chunked
+WY form).
 
 The C part is built with plain ``gcc -O2 -fopenmp`` (no fast-math) into
 ``oracle/libgdn_oracle.so``.
@@ -59,6 +61,10 @@ def _load():
     lib.gdn_oracle_out_norm.argtypes = [P, P, P, P, ctypes.c_double, ctypes.c_int64,
                                         ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int]
     lib.gdn_oracle_out_norm.restype = ctypes.c_int
+    lib.gdn_oracle_pre.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_double,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, P, P, P, P, P, P]
+    lib.gdn_oracle_pre.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.argtypes = []
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -155,3 +161,38 @@ def out_norm(o, z, w, eps: float, heads=None, threads: int = 0, return_preroundi
     if return_prerounding:
         return y, y64.reshape(shape)
     return y
+
+
+def pre(x, conv_w, hist, n_k_heads, n_v_heads, dk=128, dv=128, a=None, b=None, A_log=None,
+        dt_bias=None, activation=1, eps=1e-6):
+    """O3, the step before the recurrence, on float32 inputs in the library layout:
+    x [T][2*Hk*dk + Hv*dv] (q | k | v channels), conv_w [C][4], hist [3][C]; optionally
+    a, b [T][Hv] and A_log, dt_bias [Hv] for the gate and beta.  Returns a dict of float64
+    arrays: q, k [T][Hk][dk]; v [T][Hv][dv]; hist [3][C]; and g, beta [T][Hv] when the gate
+    inputs are given."""
+    lib = _load()
+    x = _c(x, np.float32); w = _c(conv_w, np.float32); hs = _c(hist, np.float32)
+    T, C = x.shape
+    assert C == 2 * n_k_heads * dk + n_v_heads * dv
+    assert w.shape == (C, 4) and hs.shape == (3, C)
+    out = {"q": np.empty((T, n_k_heads, dk)), "k": np.empty((T, n_k_heads, dk)),
+           "v": np.empty((T, n_v_heads, dv)), "hist": np.empty((3, C))}
+    gates = a is not None
+    if gates:
+        a = _c(a, np.float32); b = _c(b, np.float32)
+        A_log = _c(A_log, np.float32); dt_bias = _c(dt_bias, np.float32)
+        assert a.shape == (T, n_v_heads) and b.shape == (T, n_v_heads)
+        assert A_log.shape == (n_v_heads,) and dt_bias.shape == (n_v_heads,)
+        out["g"] = np.empty((T, n_v_heads))
+        out["beta"] = np.empty((T, n_v_heads))
+    nul = ctypes.c_void_p(0)
+    rc = lib.gdn_oracle_pre(_ptr(x), _ptr(w), _ptr(hs),
+                            _ptr(a) if gates else nul, _ptr(b) if gates else nul,
+                            _ptr(A_log) if gates else nul, _ptr(dt_bias) if gates else nul,
+                            int(activation), float(eps), T, n_k_heads, n_v_heads, dk, dv,
+                            _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]),
+                            _ptr(out["g"]) if gates else nul,
+                            _ptr(out["beta"]) if gates else nul, _ptr(out["hist"]))
+    if rc != 0:
+        raise ValueError("gdn_oracle_pre rejected its arguments")
+    return out

@@ -209,3 +209,103 @@ int gdn_oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/*
+ * O3, the step before the recurrence ("Round 20 Track C Audit: gdn_pre ...", section 1,
+ * the key-head branch of gdn_pre and its helper gp_conv; section 2 lists its outputs: the
+ * normalised q and k, the convolved v, the gate and beta, and the conv history).
+ *
+ * x is the projection output [T][C] with C = 2*Hk*dk + Hv*dv channels per token: the q
+ * channels of key head kh at kh*dk, the k channels of key head kh at (Hk + kh)*dk, the v
+ * channels of value head h at 2*Hk*dk + h*dv (the page's key-head branch addresses q at
+ * kh*S and k at (hk_n + kh)*S within a token's row).  Per token t and channel c:
+ *
+ *   xe      = the 3 history rows (the conv inputs of the 3 tokens before the call, oldest
+ *             first) followed by the T rows of x
+ *   u[t][c] = sum_{j=0..3} w[c][j] * xe[t + j][c]    (4-tap causal conv: the page loads
+ *             the four taps of a channel as one float4 and applies them to the rows at
+ *             t-3, t-2, t-1, t; tap 3 multiplies the current token)
+ *   u       = act(u)   (activation == 1: SiLU, u / (1 + e^-u); activation == 0: none.
+ *             The page does not name the activation: a reading, parity unpinned)
+ *   q[t][kh][i] = u_q[i] / sqrt(sum_i u_q[i]^2 + eps) / sqrt(dk)
+ *   k[t][kh][i] = u_k[i] / sqrt(sum_i u_k[i]^2 + eps)
+ *             (L2 normalisation over the head's dk channels; the q scale 1/sqrt(dk) of the
+ *             workload's q.  The form of eps is a reading, parity unpinned)
+ *   v[t][h][j]  = u_v[j]
+ *   hist_out[j] = xe[T + j], j = 0, 1, 2   (the conv inputs of the call's last 3 tokens,
+ *             taken from hist_in where the call has fewer than 3 tokens)
+ *   g[t][h]     = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *   beta[t][h]  = 1 / (1 + exp(-b[t][h]))
+ *             (the page prints no gate or beta formula: the common gated-DeltaNet form is
+ *             taken as a reading, parity unpinned; it gives g < 0 and beta in (0, 1))
+ *
+ * Inputs are float32 (the arrays the GPU receives) and widened to double; outputs are
+ * double.  a, b, A_log, dt_bias, g and beta may all be NULL (no gate and beta).
+ * Returns 0, or -1 on a bad argument.
+ */
+static double softplus_f64(double z) {
+  return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z)); /* log(1 + e^z), both branches exact */
+}
+
+int gdn_oracle_pre(const float* x, const float* w, const float* hist_in, const float* a,
+                   const float* b, const float* A_log, const float* dt_bias, int activation,
+                   double eps, int64_t T, int n_k_heads, int n_v_heads, int dk, int dv,
+                   double* q, double* k, double* v, double* g, double* beta,
+                   double* hist_out) {
+  if (T < 0 || n_k_heads < 1 || n_v_heads < 1 || dk < 1 || dv < 1) return -1;
+  if (activation != 0 && activation != 1) return -1;
+  const int gates = a != NULL;
+  if (gates && (!b || !A_log || !dt_bias || !g || !beta)) return -1;
+  const int64_t C = 2 * (int64_t)n_k_heads * dk + (int64_t)n_v_heads * dv;
+  double* u = (double*)malloc(sizeof(double) * (size_t)C);
+  for (int64_t t = 0; t < T; ++t) {
+    /* the conv over the extended sequence, then the activation */
+    for (int64_t c = 0; c < C; ++c) {
+      double s = 0.0;
+      for (int j = 0; j < 4; ++j) {
+        const int64_t r = t + j; /* row of xe */
+        const double xv = r < 3 ? (double)hist_in[r * C + c] : (double)x[(r - 3) * C + c];
+        s += (double)w[c * 4 + j] * xv;
+      }
+      u[c] = activation ? s / (1.0 + exp(-s)) : s;
+    }
+    /* q and k: L2 normalisation per key head, q also scaled by 1/sqrt(dk) */
+    for (int kh = 0; kh < n_k_heads; ++kh) {
+      const double* uq = u + (int64_t)kh * dk;
+      const double* uk = u + ((int64_t)n_k_heads + kh) * dk;
+      double sq = 0.0, sk = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        sq += uq[i] * uq[i];
+        sk += uk[i] * uk[i];
+      }
+      const double rq = 1.0 / sqrt(sq + eps) / sqrt((double)dk);
+      const double rk = 1.0 / sqrt(sk + eps);
+      double* qo = q + (t * n_k_heads + kh) * dk;
+      double* ko = k + (t * n_k_heads + kh) * dk;
+      for (int i = 0; i < dk; ++i) {
+        qo[i] = uq[i] * rq;
+        ko[i] = uk[i] * rk;
+      }
+    }
+    for (int h = 0; h < n_v_heads; ++h) {
+      const double* uv = u + 2 * (int64_t)n_k_heads * dk + (int64_t)h * dv;
+      double* vo = v + (t * n_v_heads + h) * dv;
+      for (int j = 0; j < dv; ++j) vo[j] = uv[j];
+    }
+    if (gates) {
+      for (int h = 0; h < n_v_heads; ++h) {
+        const int64_t e = t * n_v_heads + h;
+        g[e] = -exp((double)A_log[h]) * softplus_f64((double)a[e] + (double)dt_bias[h]);
+        beta[e] = 1.0 / (1.0 + exp(-(double)b[e]));
+      }
+    }
+  }
+  /* the conv inputs of the last 3 rows of xe */
+  for (int j = 0; j < 3; ++j) {
+    const int64_t r = T + j;
+    for (int64_t c = 0; c < C; ++c)
+      hist_out[j * C + c] = r < 3 ? (double)hist_in[r * C + c] : (double)x[(r - 3) * C + c];
+  }
+  free(u);
+  return 0;
+}

@@ -2,7 +2,9 @@
 
 Each case plants one mistake in a copy of the oracle's C source (a dropped decay, a wrong
 sign, a dropped beta, the wrong key-head map, a transposed state read, a norm without
-epsilon or with a sum instead of a mean, a SiLU-style gate, a truncating FP16 encoder),
+epsilon or with a sum instead of a mean, a SiLU-style gate, a truncating FP16 encoder; in
+the step before the recurrence, reversed conv taps or history rows, a missing q scale, k
+normalised by q's norm, a wrong-signed SiLU, a positive gate, a stale history out),
 builds it with the oracle's own compiler line, and runs the pins against it in a fresh
 process through ``ORACLE_LIB_OVERRIDE``: at least one pin must fail.  The oracle under
 test is never modified; the copies live in a temporary directory.
@@ -17,8 +19,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "gdn_oracle.c")
 
-RECURRENCE_PINS = "not dense_form_full and not norm and not f16"
-NORM_PINS = "norm or f16"
+RECURRENCE_PINS = "not dense_form_full and not norm and not f16 and not pre"
+NORM_PINS = "(norm or f16) and not pre"
+PRE_PINS = "pre"
 
 # name: (exact text in the oracle, planted replacement, pins expected to catch it)
 MUTANTS = {
@@ -41,6 +44,22 @@ MUTANTS = {
                        "const double val = orow[j] * rs * wrow[j] * gate * zrow[j];", NORM_PINS),
     "f16_truncating": ("if (rem > halfway || (rem == halfway && (qv & 1))) ++qv;",
                        "if (0) ++qv;", NORM_PINS),
+    "pre_taps_reversed": ("s += (double)w[c * 4 + j] * xv;",
+                          "s += (double)w[c * 4 + 3 - j] * xv;", PRE_PINS),
+    "pre_history_rows_reversed": ("const double xv = r < 3 ? (double)hist_in[r * C + c]",
+                                  "const double xv = r < 3 ? (double)hist_in[(2 - r) * C + c]",
+                                  PRE_PINS),
+    "pre_q_without_scale": ("const double rq = 1.0 / sqrt(sq + eps) / sqrt((double)dk);",
+                            "const double rq = 1.0 / sqrt(sq + eps);", PRE_PINS),
+    "pre_k_normalised_by_q": ("const double rk = 1.0 / sqrt(sk + eps);",
+                              "const double rk = 1.0 / sqrt(sq + eps);", PRE_PINS),
+    "pre_silu_wrong_sign": ("u[c] = activation ? s / (1.0 + exp(-s)) : s;",
+                            "u[c] = activation ? s / (1.0 + exp(s)) : s;", PRE_PINS),
+    "pre_gate_positive": ("g[e] = -exp((double)A_log[h])", "g[e] = exp((double)A_log[h])",
+                          PRE_PINS),
+    "pre_history_out_stale": ("hist_out[j * C + c] = r < 3 ? (double)hist_in[r * C + c]",
+                              "hist_out[j * C + c] = r < 3 ? (double)hist_in[j * C + c]",
+                              PRE_PINS),
 }
 
 
@@ -69,7 +88,7 @@ def test_pins_catch_planted_mistake(name, source, tmp_path):
     assert r.returncode == 1 and "failed" in r.stdout, (name, summary)
 
 
-@pytest.mark.parametrize("pins", [RECURRENCE_PINS, NORM_PINS])
+@pytest.mark.parametrize("pins", [RECURRENCE_PINS, NORM_PINS, PRE_PINS])
 def test_pins_pass_on_unmodified_copy(pins, source, tmp_path):
     """Control: the same build and run of the unmodified source passes, so a failure above
     comes from the planted mistake."""

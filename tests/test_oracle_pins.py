@@ -371,3 +371,151 @@ def test_norm_output_is_rounded_prerounding(oracle_mod):
     w = 1 + 0.1 * rng.standard_normal((3, 128))
     y, y64 = oracle_mod.out_norm(o, z, w, 1e-6, return_prerounding=True)
     assert np.array_equal(y.view(np.uint16), y64.astype(np.float16).view(np.uint16))
+
+
+# --- O3, the step before the recurrence ("Round 20 Track C Audit: gdn_pre ...", section 1)
+# Channel layout of a token's row: q of key head kh at kh*dk, k of key head kh at
+# (Hk + kh)*dk, v of value head h at 2*Hk*dk + h*dv.
+
+def _pre_small(T, seed=0, hk=2, hv=4, dk=128, dv=128, zero_history=False):
+    from linear_attention_recurrence_gated_amd.inputs import make_pre_inputs
+    return make_pre_inputs(T, seed=seed, n_k_heads=hk, n_v_heads=hv, dk=dk, dv=dv,
+                           zero_history=zero_history)
+
+
+def _pre_run(oracle_mod, x, hk=2, hv=4, activation=1, eps=1e-6, gates=True, dk=128, dv=128):
+    kw = dict(a=x["a"], b=x["b"], A_log=x["A_log"], dt_bias=x["dt_bias"]) if gates else {}
+    return oracle_mod.pre(x["x"], x["conv_w"], x["hist"], hk, hv, dk=dk, dv=dv,
+                          activation=activation, eps=eps, **kw)
+
+
+def _numpy_conv(x, w, hist):
+    """The 4-tap causal conv of every channel with numpy.convolve (a library routine) over
+    the history rows followed by x; tap 3 multiplies the current token."""
+    xe = np.concatenate([hist, x]).astype(np.float64)
+    T = x.shape[0]
+    out = np.empty((T, x.shape[1]))
+    for c in range(x.shape[1]):
+        out[:, c] = np.convolve(xe[:, c], w[c, ::-1].astype(np.float64), mode="valid")
+    return out
+
+
+@pytest.mark.parametrize("activation", [0, 1])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 9])
+def test_pre_matches_numpy_convolution(oracle_mod, T, activation):
+    """v is the conv (then the activation) of its channels; q and k are the conv of theirs
+    normalised by numpy's vector norm (eps = 0), q also scaled by 1/sqrt(dk)."""
+    from scipy.special import expit
+    hk, hv, dk, dv = 2, 3, 128, 128
+    x = _pre_small(T, seed=3 + T, hk=hk, hv=hv)
+    r = _pre_run(oracle_mod, x, hk=hk, hv=hv, activation=activation, eps=0.0, gates=False)
+    u = _numpy_conv(x["x"], x["conv_w"], x["hist"])
+    if activation:
+        u = u * expit(u)
+    uq = u[:, :hk * dk].reshape(T, hk, dk)
+    uk = u[:, hk * dk:2 * hk * dk].reshape(T, hk, dk)
+    uv = u[:, 2 * hk * dk:].reshape(T, hv, dv)
+    qn = uq / np.linalg.norm(uq, axis=-1, keepdims=True) / np.sqrt(dk)
+    kn = uk / np.linalg.norm(uk, axis=-1, keepdims=True)
+    assert rel_err(r["v"], uv) <= 1e-14
+    assert rel_err(r["q"], qn) <= 1e-14
+    assert rel_err(r["k"], kn) <= 1e-14
+
+
+def test_pre_impulse_response(oracle_mod):
+    """A unit impulse in one v channel at token t0, from a zero history and no activation:
+    that channel's outputs at t0, t0+1, t0+2, t0+3 are taps 3, 2, 1, 0; everything else 0."""
+    hk, hv, dk, dv, T, t0 = 2, 3, 128, 128, 9, 2
+    x = _pre_small(T, seed=1, hk=hk, hv=hv, zero_history=True)
+    x["x"][:] = 0.0
+    h, j = 1, 37
+    c = 2 * hk * dk + h * dv + j
+    x["x"][t0, c] = 1.0
+    r = _pre_run(oracle_mod, x, hk=hk, hv=hv, activation=0, gates=False)
+    want = np.zeros((T, hv, dv))
+    for d in range(4):
+        want[t0 + d, h, j] = x["conv_w"][c, 3 - d]
+    assert np.array_equal(r["v"], want)
+    assert not r["q"].any() and not r["k"].any()
+
+
+@pytest.mark.parametrize("T1", [1, 2, 3, 5])
+def test_pre_split_invariance(oracle_mod, T1):
+    """Two calls chained through the history give the bits of one call."""
+    hk, hv = 2, 4
+    x = _pre_small(12, seed=5, hk=hk, hv=hv)
+    full = _pre_run(oracle_mod, x, hk=hk, hv=hv)
+    first = dict(x, x=x["x"][:T1], a=x["a"][:T1], b=x["b"][:T1])
+    r1 = _pre_run(oracle_mod, first, hk=hk, hv=hv)
+    second = dict(x, x=x["x"][T1:], a=x["a"][T1:], b=x["b"][T1:],
+                  hist=r1["hist"].astype(np.float32))
+    assert np.array_equal(r1["hist"].astype(np.float32).astype(np.float64), r1["hist"])
+    r2 = _pre_run(oracle_mod, second, hk=hk, hv=hv)
+    for n in ("q", "k", "v", "g", "beta"):
+        assert np.array_equal(np.concatenate([r1[n], r2[n]]), full[n]), n
+    assert np.array_equal(r2["hist"], full["hist"])
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 3, 7])
+def test_pre_history_rows(oracle_mod, T):
+    """The history out is the last three rows of the history in followed by x."""
+    x = _pre_small(T, seed=8)
+    r = _pre_run(oracle_mod, x)
+    xe = np.concatenate([x["hist"], x["x"]]).astype(np.float64)
+    assert np.array_equal(r["hist"], xe[-3:])
+
+
+def test_pre_unit_norm(oracle_mod):
+    """With eps = 0 every k row has unit L2 norm and every q row norm 1/sqrt(dk)."""
+    x = _pre_small(16, seed=9)
+    r = _pre_run(oracle_mod, x, eps=0.0)
+    assert np.allclose(np.linalg.norm(r["k"], axis=-1), 1.0, rtol=0, atol=1e-15)
+    assert np.allclose(np.linalg.norm(r["q"], axis=-1) * np.sqrt(128), 1.0, rtol=0, atol=1e-15)
+
+
+def test_pre_eps_shrinks_the_norm(oracle_mod):
+    """A positive eps gives |k| = |u| / sqrt(|u|^2 + eps) < 1 (the closed form of the
+    normalisation), checked against the eps = 0 direction."""
+    x = _pre_small(6, seed=10)
+    r0 = _pre_run(oracle_mod, x, eps=0.0)
+    eps = 0.3
+    r = _pre_run(oracle_mod, x, eps=eps)
+    u = _numpy_conv(x["x"], x["conv_w"], x["hist"])
+    u = u * (1.0 / (1.0 + np.exp(-u)))
+    uk = u[:, 2 * 128:4 * 128].reshape(6, 2, 128)
+    nu = np.linalg.norm(uk, axis=-1, keepdims=True)
+    assert rel_err(r["k"], r0["k"] * nu / np.sqrt(nu * nu + eps)) <= 1e-14
+
+
+def test_pre_gate_and_beta_closed_forms(oracle_mod):
+    """beta = the logistic function of b (scipy's expit); g = -e^{A_log} log(1 + e^{a +
+    dt_bias}) (numpy's logaddexp); g < 0 and beta in (0, 1)."""
+    from scipy.special import expit
+    x = _pre_small(50, seed=11)
+    x["a"][0] = 40.0
+    x["a"][1] = -40.0
+    r = _pre_run(oracle_mod, x)
+    beta = expit(x["b"].astype(np.float64))
+    g = -np.exp(x["A_log"].astype(np.float64)) * np.logaddexp(
+        0.0, x["a"].astype(np.float64) + x["dt_bias"].astype(np.float64))
+    assert np.allclose(r["beta"], beta, rtol=1e-15, atol=0)
+    assert np.allclose(r["g"], g, rtol=1e-14, atol=0)
+    assert (r["g"] < 0).all() and (r["beta"] > 0).all() and (r["beta"] < 1).all()
+
+
+def test_pre_channel_layout(oracle_mod):
+    """A spike in the q channels of key head 1 moves only q of key head 1; in the k channels
+    of key head 0 only k of key head 0; in the v channels of value head 2 only v of value
+    head 2 (the page's row layout: q heads, then k heads, then v heads)."""
+    hk, hv, dk, dv = 2, 3, 128, 128
+    base = _pre_small(5, seed=12, hk=hk, hv=hv)
+    r0 = _pre_run(oracle_mod, base, hk=hk, hv=hv, gates=False)
+    for c, (name, head) in ((1 * dk + 5, ("q", 1)), (hk * dk + 9, ("k", 0)),
+                            (2 * hk * dk + 2 * dv + 3, ("v", 2))):
+        x = dict(base, x=base["x"].copy())
+        x["x"][4, c] += 3.0
+        r = _pre_run(oracle_mod, x, hk=hk, hv=hv, gates=False)
+        for n in ("q", "k", "v"):
+            diff = np.abs(r[n] - r0[n]).max(axis=(0, 2))
+            for hh in range(diff.size):
+                assert (diff[hh] > 0) == (n == name and hh == head), (c, n, hh)
