@@ -193,7 +193,8 @@ def _median(xs):
 
 def context_workloads(gdn, d, hip, stream, dev, runs=3):
     """Times (HIP events on the launch stream, medians of `runs` after one unmeasured run)
-    of the T = 8192 sequential layer and of the 36-layer stack at T = 2048.  The stack's
+    of the T = 8192 sequential layer, of the 36-layer stack at T = 2048, and of the step
+    before the recurrence (gdn_pre) at the bench's T.  The stack's
     layers get inputs of their own, drawn on the device with the distributions of
     make_inputs (their values do not change the work), so no layer finds another's data
     in the caches."""
@@ -256,6 +257,39 @@ def context_workloads(gdn, d, hip, stream, dev, runs=3):
     out["stack36_T2048_ms"] = round(_median(stack), 4)
     out["stack36_T2048_us_per_token_layer"] = round(_median(stack) * 1e3 / (L * T2), 6)
     del layers
+    torch.cuda.empty_cache()
+
+    # The step before the recurrence (gdn_pre) at T = 32768: the 4-tap conv with its
+    # history, the q/k normalisation and the gate/beta formation, HBM-bound.
+    Tp = d["q"].shape[0]
+    C = (2 * Hk + Hv) * D
+    gen.manual_seed(2000)
+    pin = dict(x=torch.randn((Tp, C), device=dev, generator=gen),
+               conv_w=0.5 * torch.randn((C, 4), device=dev, generator=gen),
+               hist=torch.randn((3, C), device=dev, generator=gen),
+               a=torch.randn((Tp, Hv), device=dev, generator=gen),
+               b=torch.randn((Tp, Hv), device=dev, generator=gen),
+               A_log=torch.log(1.0 + 15.0 * torch.rand(Hv, device=dev, generator=gen)),
+               dt_bias=0.5 * torch.randn(Hv, device=dev, generator=gen))
+    pout = dict(hist_out=torch.empty_like(pin["hist"]),
+                q=torch.empty((Tp, Hk, D), device=dev), k=torch.empty((Tp, Hk, D), device=dev),
+                v=torch.empty((Tp, Hv, D), device=dev), g=torch.empty((Tp, Hv), device=dev),
+                beta=torch.empty((Tp, Hv), device=dev))
+    pre_ms = []
+    for i in range(runs + 2):
+        evs = hip.create(2)
+        hip.record(evs[0], stream.cuda_stream)
+        gdn.pre(pin["x"], pin["conv_w"], pin["hist"], Hk, Hv, a=pin["a"], b=pin["b"],
+                A_log=pin["A_log"], dt_bias=pin["dt_bias"], activation=1, eps=1e-6, **pout)
+        hip.record(evs[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            pre_ms.append(hip.elapsed_ms(evs[0], evs[1]))
+        hip.destroy(evs)
+    pre_bytes = Tp * (2 * C * 4 + 4 * Hv * 4) + C * 16 + 2 * 3 * C * 4
+    out["pre_T32768_us_per_token"] = round(_median(pre_ms) * 1e3 / Tp, 6)
+    out["pre_T32768_hbm_GBps"] = round(pre_bytes / (_median(pre_ms) * 1e-3) / 1e9, 1)
+    del pin, pout
     torch.cuda.empty_cache()
     return out
 

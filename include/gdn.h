@@ -205,6 +205,48 @@ int gdn_layer_chunked_timed(const float* q, const float* k, const float* v, cons
                             void* const* scan_events, int n_scan_events, void* stream);
 
 /*
+ * The step before the recurrence ("Round 20 Track C Audit: gdn_pre ...", section 1: the
+ * 4-tap causal conv of the projection output and the key-head branch that normalises q and
+ * k; section 2 lists its outputs, the normalised q and k, the convolved v, the gate and
+ * beta, and the conv history).  Per token t and channel c of x:
+ *
+ *   u[t][c]   = sum_{j=0..3} conv_w[c][j] * xe[t + j][c]
+ *               (xe = the 3 rows of hist_in, oldest first, followed by the T rows of x:
+ *               tap 3 multiplies the current token)
+ *   u         = act(u)            activation 0: none; 1: SiLU, u / (1 + e^-u)
+ *   q[t][kh]  = u_q / sqrt(sum u_q^2 + eps) / sqrt(dk)      (per key head, over dk)
+ *   k[t][kh]  = u_k / sqrt(sum u_k^2 + eps)
+ *   v[t][h]   = u_v
+ *   g[t][h]   = -exp(A_log[h]) * log(1 + exp(a[t][h] + dt_bias[h]))
+ *   beta[t][h]= 1 / (1 + exp(-b[t][h]))
+ *   hist_out  = the last 3 rows of xe (the history of the next call of the same sequence)
+ *
+ * The page shows the conv, the history and the normalised outputs but prints neither the
+ * activation, nor the form of eps, nor the gate and beta formulas: those are this
+ * library's readings (the activation is an argument).
+ *
+ *   x          [T][C] fp32, C = (2 n_k_heads + n_v_heads) * 128: the q channels of key head
+ *              kh at kh*128, the k channels of key head kh at (n_k_heads + kh)*128, the v
+ *              channels of value head h at (2 n_k_heads + h)*128.
+ *   conv_w     [C][4], hist_in [3][C]: read.  hist_out [3][C]: written; it must not overlap
+ *              hist_in (pass a second buffer and swap them between calls).
+ *   a, b       [T][n_v_heads], A_log, dt_bias [n_v_heads]: read.  g, beta [T][n_v_heads]:
+ *              written.  These six are all given or all NULL (then no gate and beta).
+ *   q, k       [T][n_k_heads][dk], v [T][n_v_heads][dv]: written (the recurrence's layout).
+ *   eps        >= 0 and finite; activation 0 or 1; dk = dv = 128.  Otherwise, or when the
+ *              grid would exceed 2^31 waves, GDN_ERR_BAD_SHAPE.
+ *   T = 0      copies hist_in to hist_out and writes nothing else (every pointer but the
+ *              two histories may then be NULL).
+ *   No output may overlap an input or another output.  The results are FP32: within a few
+ *   FP32 ulps of the exact values (the conv, exp and log are the correctly rounded or
+ *   1-ulp library functions).
+ */
+int gdn_pre(const float* x, const float* conv_w, const float* hist_in, float* hist_out,
+            const float* a, const float* b, const float* A_log, const float* dt_bias,
+            int activation, float eps, float* q, float* k, float* v, float* g, float* beta,
+            int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* stream);
+
+/*
  * gdn_layer_chunked for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same validation, the
  * same kernels and the same results bit for bit as gdn_layer_chunked, but without a

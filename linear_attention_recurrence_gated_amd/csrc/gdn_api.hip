@@ -404,6 +404,59 @@ int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint
   return e == hipSuccess ? GDN_OK : hip_fail(e);
 }
 
+int gdn_pre(const float* x, const float* conv_w, const float* hist_in, float* hist_out,
+            const float* a, const float* b, const float* A_log, const float* dt_bias,
+            int activation, float eps, float* q, float* k, float* v, float* g, float* beta,
+            int64_t T, int n_k_heads, int n_v_heads, int dk, int dv, void* stream) {
+  if (T < 0 || T >= ((int64_t)1 << 31) || n_k_heads < 1 || n_v_heads < 1)
+    return GDN_ERR_BAD_SHAPE;
+  if (dk != gdn::kDim || dv != gdn::kDim) return GDN_ERR_BAD_SHAPE;
+  if (n_k_heads > 65536 || n_v_heads > 65536) return GDN_ERR_BAD_SHAPE;
+  if (activation != 0 && activation != 1) return GDN_ERR_BAD_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GDN_ERR_BAD_SHAPE;
+  const size_t f = sizeof(float);
+  const size_t C = (size_t)(2 * n_k_heads + n_v_heads) * gdn::kDim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {  // only the history: every other pointer may be NULL (empty tensors)
+    if (!hist_in || !hist_out) return GDN_ERR_NULL_POINTER;
+    if (!aligned16(hist_in) || !aligned16(hist_out)) return GDN_ERR_MISALIGNED;
+    if (overlap(range_of(hist_in, 3 * C * f), range_of(hist_out, 3 * C * f)))
+      return GDN_ERR_ALIASING;
+    const hipError_t e = hipMemcpyAsync(hist_out, hist_in, 3 * C * f, hipMemcpyDeviceToDevice, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e);
+  }
+  const bool gates = a || b || A_log || dt_bias || g || beta;
+  if (gates && !(a && b && A_log && dt_bias && g && beta)) return GDN_ERR_NULL_POINTER;
+  if (!x || !conv_w || !hist_in || !hist_out || !q || !k || !v) return GDN_ERR_NULL_POINTER;
+  const void* ptrs[] = {x, conv_w, hist_in, hist_out, a, b, A_log, dt_bias, q, k, v, g, beta};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+  const size_t qk_b = (size_t)T * n_k_heads * gdn::kDim * f;
+  const size_t v_b = (size_t)T * n_v_heads * gdn::kDim * f, gb_b = (size_t)T * n_v_heads * f;
+  const Range in[] = {range_of(x, (size_t)T * C * f), range_of(conv_w, C * 4 * f),
+                      range_of(hist_in, 3 * C * f), range_of(a, a ? gb_b : 0),
+                      range_of(b, b ? gb_b : 0), range_of(A_log, A_log ? n_v_heads * f : 0),
+                      range_of(dt_bias, dt_bias ? n_v_heads * f : 0)};
+  const Range out[] = {range_of(hist_out, 3 * C * f), range_of(q, q ? qk_b : 0),
+                       range_of(k, k ? qk_b : 0), range_of(v, v ? v_b : 0),
+                       range_of(g, g ? gb_b : 0), range_of(beta, beta ? gb_b : 0)};
+  for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return GDN_ERR_ALIASING;
+    for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
+      if (overlap(out[i], out[j])) return GDN_ERR_ALIASING;
+  }
+  // the grid: one wave per (64-token run, 128-channel head block), one thread per gate
+  // (the kernel indexes waves and workgroups with 32-bit integers)
+  const int64_t waves = ((T + 63) / 64) * (int64_t)(2 * n_k_heads + n_v_heads);
+  const int64_t blocks = (waves + 3) / 4 + (gates ? (T * n_v_heads + 255) / 256 : 0);
+  if (waves >= ((int64_t)1 << 31) || blocks >= ((int64_t)1 << 31)) return GDN_ERR_BAD_SHAPE;
+  gdn::PreArgs pa{x, conv_w, hist_in, hist_out, gates ? a : nullptr, b, A_log, dt_bias,
+                  q, k, v, g, beta, activation, eps, (int)T, n_k_heads, n_v_heads};
+  const hipError_t e = gdn::launch_pre(pa, s);
+  return e == hipSuccess ? GDN_OK : hip_fail(e);
+}
+
 const char* gdn_status_string(int status) {
   switch (status) {
     case GDN_OK: return "ok";

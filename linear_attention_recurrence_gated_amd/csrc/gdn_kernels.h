@@ -62,6 +62,27 @@ struct NormArgs {
   int n_v_heads;
 };
 
+struct PreArgs {
+  const float* x;        // [T][C], C = (2 n_k_heads + n_v_heads) * 128: q | k | v channels
+  const float* conv_w;   // [C][4]
+  const float* hist_in;  // [3][C]
+  float* hist_out;       // [3][C]
+  const float* a;        // [T][n_v_heads] raw gate (NULL: no gate and beta)
+  const float* b;        // [T][n_v_heads] raw beta
+  const float* A_log;    // [n_v_heads]
+  const float* dt_bias;  // [n_v_heads]
+  float* q;              // [T][n_k_heads][128]
+  float* k;              // [T][n_k_heads][128]
+  float* v;              // [T][n_v_heads][128]
+  float* g;              // [T][n_v_heads]
+  float* beta;           // [T][n_v_heads]
+  int activation;        // 0: none, 1: SiLU
+  float eps;
+  int T;
+  int n_k_heads;
+  int n_v_heads;
+};
+
 // Compute units of the device that `stream` runs on (queried once per device, then cached).
 hipError_t device_cu_count(hipStream_t stream, int* cus);
 
@@ -74,5 +95,6 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_next,
                                    const NormArgs* norm_prev, hipStream_t stream);
 hipError_t launch_out_norm(const NormArgs& a, hipStream_t stream);
+hipError_t launch_pre(const PreArgs& a, hipStream_t stream);
 
 }  // namespace gdn

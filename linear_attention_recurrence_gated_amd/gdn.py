@@ -35,6 +35,8 @@ SIGNATURES = {
                                      _I, _I, _I, _P, _SZ, _P, _I, _P]),
     "gdn_layer_chunked_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I64,
                                        _I, _I, _I, _I, _P]),
+    "gdn_pre": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _P, _I64, _I, _I,
+                     _I, _I, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
     "gdn_last_hip_error": (_I, []),
     "gdn_abi_version": (_I, []),
@@ -260,6 +262,73 @@ def layer_chunked(q, k, v, g, beta, state_in, z, w, eps=1e-6, state_out=None, o=
         st = lib().gdn_layer_chunked_timed(*args, arr, len(scan_events), _stream(stream, q.device))
         _check("gdn_layer_chunked_timed", st)
     return y, o, state_out
+
+
+def check_pre_shapes(x, conv_w, hist_in, n_k_heads, n_v_heads, dk=128, dv=128, hist_out=None,
+                     a=None, b=None, A_log=None, dt_bias=None, q=None, k=None, v=None, g=None,
+                     beta=None):
+    """Shapes of gdn_pre's operands against T from x and the head counts (ValueError on the
+    first mismatch; only ``.shape`` is read).  Returns (T, C)."""
+    if len(x.shape) != 2:
+        raise ValueError("x must be [T][C]; got %s" % (tuple(x.shape),))
+    T, C = x.shape
+    if C != (2 * n_k_heads) * dk + n_v_heads * dv:
+        raise ValueError("x has %d channels, expected 2*%d*%d + %d*%d"
+                         % (C, n_k_heads, dk, n_v_heads, dv))
+    want = {"conv_w": (conv_w, (C, 4)), "hist_in": (hist_in, (3, C)),
+            "hist_out": (hist_out, (3, C)), "a": (a, (T, n_v_heads)), "b": (b, (T, n_v_heads)),
+            "A_log": (A_log, (n_v_heads,)), "dt_bias": (dt_bias, (n_v_heads,)),
+            "q": (q, (T, n_k_heads, dk)), "k": (k, (T, n_k_heads, dk)),
+            "v": (v, (T, n_v_heads, dv)), "g": (g, (T, n_v_heads)), "beta": (beta, (T, n_v_heads))}
+    for name, (t, shape) in want.items():
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+    return T, C
+
+
+def pre(x, conv_w, hist_in, n_k_heads, n_v_heads, a=None, b=None, A_log=None, dt_bias=None,
+        activation=1, eps=1e-6, hist_out=None, q=None, k=None, v=None, g=None, beta=None,
+        stream=None):
+    """gdn_pre: the 4-tap causal conv with its history, the q/k normalisation and (when a,
+    b, A_log, dt_bias are given) the gate and beta.  Returns a dict with q, k, v, hist_out
+    and, with the gate inputs, g and beta."""
+    for t, n in ((x, "x"), (conv_w, "conv_w"), (hist_in, "hist_in")):
+        _f32(t, n)
+    gates = a is not None
+    if gates:
+        for t, n in ((a, "a"), (b, "b"), (A_log, "A_log"), (dt_bias, "dt_bias")):
+            _f32(t, n)
+    dk = dv = 128
+    T, C = check_pre_shapes(x, conv_w, hist_in, n_k_heads, n_v_heads, dk, dv, hist_out, a, b,
+                            A_log, dt_bias, q, k, v, g, beta)
+    dev = x.device
+    if hist_out is None:
+        hist_out = torch.empty_like(hist_in)
+    if q is None:
+        q = torch.empty((T, n_k_heads, dk), dtype=torch.float32, device=dev)
+    if k is None:
+        k = torch.empty((T, n_k_heads, dk), dtype=torch.float32, device=dev)
+    if v is None:
+        v = torch.empty((T, n_v_heads, dv), dtype=torch.float32, device=dev)
+    if gates and g is None:
+        g = torch.empty((T, n_v_heads), dtype=torch.float32, device=dev)
+    if gates and beta is None:
+        beta = torch.empty((T, n_v_heads), dtype=torch.float32, device=dev)
+    for t, n in ((hist_out, "hist_out"), (q, "q"), (k, "k"), (v, "v")):
+        _f32(t, n)
+    if gates:
+        _f32(g, "g"); _f32(beta, "beta")
+    st = lib().gdn_pre(_ptr(x), _ptr(conv_w), _ptr(hist_in), _ptr(hist_out),
+                       _ptr(a if gates else None), _ptr(b if gates else None),
+                       _ptr(A_log if gates else None), _ptr(dt_bias if gates else None),
+                       int(activation), float(eps), _ptr(q), _ptr(k), _ptr(v),
+                       _ptr(g if gates else None), _ptr(beta if gates else None), T, n_k_heads,
+                       n_v_heads, dk, dv, _stream(stream, dev))
+    _check("gdn_pre", st)
+    out = {"q": q, "k": k, "v": v, "hist_out": hist_out}
+    if gates:
+        out["g"], out["beta"] = g, beta
+    return out
 
 
 NOALLOC_MAX_V_HEADS = 64  # the static workspace's head count (gdn.h)

@@ -225,3 +225,47 @@ def test_auto_dispatch_validation(L):
     assert _auto(L, dict(a, o=a["q"]), T=8) == ALIAS
     assert _auto(L, a, T=16, Hv=40) == SHAPE
     assert _auto(L, dict(a, ws=0, s_out=a["s_in"]), T=0) == OK   # nothing to do
+
+
+
+def _pre_addrs(T=64, Hk=16, Hv=48):
+    C = (2 * Hk + Hv) * 128
+    a = {}
+    cur = BASE
+    for name, size in (("x", T * C * 4), ("w", C * 16), ("hi", 3 * C * 4), ("ho", 3 * C * 4),
+                       ("a", T * Hv * 4), ("b", T * Hv * 4), ("al", Hv * 4), ("dt", Hv * 4),
+                       ("q", T * Hk * 512), ("k", T * Hk * 512), ("v", T * Hv * 512),
+                       ("g", T * Hv * 4), ("beta", T * Hv * 4)):
+        a[name] = cur
+        cur += (size + MB) & ~(MB - 1)
+    return a
+
+
+def _pre(L, a, T=64, Hk=16, Hv=48, dk=128, activation=1, eps=1e-6):
+    P = ctypes.c_void_p
+    return L.gdn_pre(P(a["x"]), P(a["w"]), P(a["hi"]), P(a["ho"]), P(a["a"]), P(a["b"]),
+                     P(a["al"]), P(a["dt"]), activation, eps, P(a["q"]), P(a["k"]), P(a["v"]),
+                     P(a["g"]), P(a["beta"]), T, Hk, Hv, dk, 128, None)
+
+
+def test_pre_validation(L):
+    """gdn_pre rejects bad arguments before any device call."""
+    a = _pre_addrs()
+    no_gates = dict(a, a=0, b=0, al=0, dt=0, g=0, beta=0)
+    assert _pre(L, a, T=-1) == SHAPE
+    assert _pre(L, a, T=1 << 31) == SHAPE
+    assert _pre(L, a, dk=64) == SHAPE
+    assert _pre(L, a, Hk=0) == SHAPE
+    assert _pre(L, a, activation=2) == SHAPE
+    assert _pre(L, a, eps=-1.0) == SHAPE
+    assert _pre(L, a, eps=float("nan")) == SHAPE
+    assert _pre(L, dict(a, x=0)) == NULLP
+    assert _pre(L, dict(a, ho=0)) == NULLP
+    assert _pre(L, dict(a, q=0)) == NULLP
+    assert _pre(L, dict(a, g=0)) == NULLP                   # gate inputs given, g missing
+    assert _pre(L, dict(no_gates, a=a["a"])) == NULLP       # a alone
+    assert _pre(L, dict(a, v=a["v"] + 8)) == MISAL
+    assert _pre(L, dict(a, q=a["x"])) == ALIAS              # an output over an input
+    assert _pre(L, dict(a, ho=a["hi"])) == ALIAS            # history out over history in
+    assert _pre(L, dict(a, g=a["beta"])) == ALIAS           # two outputs over each other
+    assert _pre(L, dict(a, k=a["q"] + 256)) == ALIAS
