@@ -6,17 +6,22 @@
 // The output sum is taken from the pre-update state: o = e^{g} (S^T q) + d (k.q), which
 // is the same quantity and lets the kv sum and the output sum run side by side.
 //
-// Work split (designed for wave64 and 256 CUs, not taken from the pages):
-//  - one workgroup = one key head x 8 value columns, for all value heads of that key head
-//    (the G heads share every staged tile of q/k rows); 16 key heads x 16 column blocks =
+// Work split (designed for wave64 and 256 CUs with four SIMDs each, not taken from the
+// pages):
+//  - one workgroup = one key head x 8 value columns, for all G value heads of that key
+//    head (they share every staged tile of q/k rows); 16 key heads x 16 column blocks =
 //    256 workgroups, one per CU;
-//  - a 64-lane wave holds 4 value columns of one value head; the 16 lanes of a column (one
-//    DPP row) each own 8 of the 128 key rows (8 floats of state per lane, in VGPRs for the
-//    whole sequence); each value head of the key head has 2 waves, so the SIMDs run
-//    several waves whose dependency chains interleave;
-//  - the kv and output sums over the 128 rows are two chains of four products per lane,
-//    then four DPP steps across the 16 lanes of the row, entirely inside the wave: no LDS
-//    round trip, no barrier per token;
+//  - a 64-lane wave holds 2 value columns of one value head, 32 lanes per column (two DPP
+//    rows), each lane owning 4 of the 128 key rows (4 floats of state in VGPRs for the
+//    whole sequence).  A value head has 4 waves, so a workgroup has 4G waves: for G = 3,
+//    12 waves, exactly 3 per SIMD, which keeps every SIMD equally loaded and gives each
+//    three independent dependency chains to interleave;
+//  - the kv and output sums over the 128 rows are chains of four products per lane, four
+//    DPP steps inside each row of 16 lanes, then one exchange between the two rows of a
+//    column for both sums at once (v_permlane16_swap trades the kv row sums of the odd rows
+//    for the output row sums of the even rows, so after one add the even rows hold the kv
+//    sum and the odd rows the output sum, and one DPP row broadcast copies the kv sum to
+//    the odd rows): no LDS round trip and no barrier per token;
 //  - the inputs of 16 tokens (q/k rows of the key head, the block's v columns, e^{g},
 //    beta and k.q) are staged in double-buffered LDS; the next tile's global loads are in
 //    flight while the current tile computes; one barrier per 16 tokens.
@@ -29,9 +34,9 @@ namespace {
 constexpr int TB = 16;    // tokens per staged tile
 constexpr int COLS = 8;   // value columns per workgroup
 constexpr int NT = 256;   // threads that stage the q/k rows
-constexpr int RPL = 8;    // key rows per lane: 16 lanes per column
+constexpr int RPL = 4;    // key rows per lane: 32 lanes per column
 template <int G>
-constexpr int seq_threads() { return 128 * (G < 2 ? 2 : G); }  // 2 waves per value head
+constexpr int seq_threads() { return 256 * G; }  // 4 waves per value head
 constexpr int NCB = kDim / COLS;  // column blocks per key head
 
 template <int G>
@@ -41,7 +46,9 @@ struct SeqSmem {
   float v[2][TB][G][COLS];
   float2 ab[2][TB][G];  // (e^{g}, beta)
   float kq[2][TB];      // k.q of the key head
-  float o[2][TB][G][COLS];
+  // outputs: [..][1][col] from the odd row of each column (where the output sum lands),
+  // [..][0][col] written and never read by the even row, so no lane needs a branch
+  float o[2][TB][G][2][COLS];
 };
 
 // One thread's share of a tile's inputs, in registers until written to LDS.
@@ -122,7 +129,7 @@ __device__ __forceinline__ void store_outputs(const SeqSmem<G>& sm, int buf, con
     const int t = t0 + tt;
     if (t < a.T)
       *reinterpret_cast<float4*>(a.o + (t * Hv + kh + m * Hk) * kDim + cb * COLS + 4 * half) =
-          *reinterpret_cast<const float4*>(&sm.o[buf][tt][m][4 * half]);
+          *reinterpret_cast<const float4*>(&sm.o[buf][tt][m][1][4 * half]);
   }
 }
 
@@ -135,6 +142,49 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// v_permlane16_swap_b32 x, y: the odd 16-lane rows of x trade places with the even rows of
+// y.  Inline assembly because this compiler's builtin for it returns one of the two
+// results for both; the s_nop gives the two wait states the instruction needs after a
+// vector-ALU write of its operands (the compiler's own lowering places the same s_nop 1).
+__device__ __forceinline__ void permlane16_swap(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+
+constexpr int DPP_ROW_BCAST15 = 0x142;  // row r <- lane 15 of row r - 1 (rows in row_mask)
+
+// One token of one wave: kc, qc are this token's k and q rows of the lane (already in
+// registers); the next token's rows are read into kn, qn while it computes.
+template <int G>
+__device__ __forceinline__ void token_step(SeqSmem<G>& sm, int buf, int tt, int tn,
+                                           const float4* kr, const float4* qr,
+                                           const float4& kc, const float4& qc, float4& kn,
+                                           float4& qn, float (&S)[RPL], int m, int cl,
+                                           int parity) {
+  constexpr int ROW4 = kDim / 4;  // float4 per token row
+  kn = kr[tn * ROW4];
+  qn = qr[tn * ROW4];
+  const float2 ab = sm.ab[buf][tt][m];
+  const float vv = sm.v[buf][tt][m][cl];
+  const float kq = sm.kq[buf][tt];
+  // four products per lane, then the 16 lanes of each DPP row
+  float pk = fmaf(S[3], kc.w, fmaf(S[2], kc.z, fmaf(S[1], kc.y, S[0] * kc.x)));
+  float pq = fmaf(S[3], qc.w, fmaf(S[2], qc.z, fmaf(S[1], qc.y, S[0] * qc.x)));
+  pk = row16_sum(pk);
+  pq = row16_sum(pq);
+  // the two rows of the column: even rows end with S^T k, odd rows with S^T q
+  permlane16_swap(pk, pq);  // by row: pk = (pk0, pq0, pk2, pq2), pq = (pk1, pq1, pk3, pq3)
+  const float sum = pk + pq;
+  const float skr = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, sum),
+                                         __builtin_bit_cast(int, sum), DPP_ROW_BCAST15, 0xA,
+                                         0xF, false));  // S^T k in every row
+  const float d = ab.y * fmaf(-ab.x, skr, vv);  // beta (v - e^g S^T k)
+  const float om = fmaf(ab.x, sum, d * kq);     // odd rows: (e^g S + k d^T)^T q
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) S[i] = fmaf((&kc.x)[i], d, ab.x * S[i]);
+  sm.o[buf][tt][m][parity][cl] = om;  // the odd row's 16 lanes hold the same value
+}
+
 template <int G>
 __device__ __forceinline__ void compute_tile(SeqSmem<G>& sm, int buf, int ntok, float (&S)[RPL],
                                              int m, int r, int cl) {
@@ -142,30 +192,24 @@ __device__ __forceinline__ void compute_tile(SeqSmem<G>& sm, int buf, int ntok, 
   // per-token scalar is read before the reductions: no LDS latency waits on the chain.
   const float4* kr = reinterpret_cast<const float4*>(&sm.k[buf][0][RPL * r]);
   const float4* qr = reinterpret_cast<const float4*>(&sm.q[buf][0][RPL * r]);
-  constexpr int ROW4 = kDim / 4;  // float4 per token row
-  float4 k0 = kr[0], k1 = kr[1], q0 = qr[0], q1 = qr[1];
-  for (int tt = 0; tt < ntok; ++tt) {
-    const int tn = min(tt + 1, ntok - 1);  // the last token of the tile re-reads its own
-    const float4 kn0 = kr[tn * ROW4], kn1 = kr[tn * ROW4 + 1];
-    const float4 qn0 = qr[tn * ROW4], qn1 = qr[tn * ROW4 + 1];
-    const float2 ab = sm.ab[buf][tt][m];
-    const float vv = sm.v[buf][tt][m][cl];
-    const float kq = sm.kq[buf][tt];
-    const float kk[RPL] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-    const float qq[RPL] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    // two chains of four products each, then the 16 lanes of the column
-    float pk = fmaf(S[3], kk[3], fmaf(S[2], kk[2], fmaf(S[1], kk[1], S[0] * kk[0]))) +
-               fmaf(S[7], kk[7], fmaf(S[6], kk[6], fmaf(S[5], kk[5], S[4] * kk[4])));
-    float pq = fmaf(S[3], qq[3], fmaf(S[2], qq[2], fmaf(S[1], qq[1], S[0] * qq[0]))) +
-               fmaf(S[7], qq[7], fmaf(S[6], qq[6], fmaf(S[5], qq[5], S[4] * qq[4])));
-    pk = row16_sum(pk);  // S^T k over the 128 rows of this column
-    pq = row16_sum(pq);  // S^T q
-    const float d = ab.y * fmaf(-ab.x, pk, vv);  // beta (v - e^g S^T k)
-    const float om = fmaf(ab.x, pq, d * kq);     // (e^g S + k d^T)^T q
+  const int parity = (threadIdx.x >> 4) & 1;  // odd DPP row of the column: the output sum
+  float4 kx[2], qx[2];
+  kx[0] = kr[0];
+  qx[0] = qr[0];
+  if (ntok == TB) {
+    // a full tile, unrolled: the two register sets alternate and every LDS offset is an
+    // immediate, so no moves or address arithmetic sit between the tokens
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) S[i] = fmaf(kk[i], d, ab.x * S[i]);
-    if (r == 0) sm.o[buf][tt][m][cl] = om;
-    k0 = kn0; k1 = kn1; q0 = qn0; q1 = qn1;
+    for (int tt = 0; tt < TB; ++tt)
+      token_step<G>(sm, buf, tt, tt + 1 < TB ? tt + 1 : tt, kr, qr, kx[tt & 1], qx[tt & 1],
+                    kx[~tt & 1], qx[~tt & 1], S, m, cl, parity);
+  } else {
+    for (int tt = 0; tt < ntok; ++tt) {
+      token_step<G>(sm, buf, tt, min(tt + 1, ntok - 1), kr, qr, kx[0], qx[0], kx[1], qx[1],
+                    S, m, cl, parity);
+      kx[0] = kx[1];
+      qx[0] = qx[1];
+    }
   }
 }
 
@@ -177,16 +221,18 @@ __global__ __launch_bounds__(seq_threads<G>()) void seq_kernel(SeqArgs a) {
   const int Hk = a.n_k_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool computes = w < 2 * G;             // (G = 1: waves 2 and 3 only stage)
-  const int m = computes ? w >> 1 : 0;         // value head of the group
-  const int cl = (w & 1) * 4 + (lane >> 4);    // column of this lane in the block
-  const int r = lane & 15;                     // owns key rows 8r .. 8r+7
+  const int m = w >> 2;                       // value head of the group
+  const int cl = (w & 3) * 2 + (lane >> 5);   // column of this lane in the block
+  const int r = lane & 31;                    // owns key rows 4r .. 4r+3
   const int j = cb * COLS + cl;
   const int h = kh + m * Hk;
 
   float S[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; ++i) S[i] = a.s_in[(h * kDim + RPL * r + i) * kDim + j];
+  // Wait for the state here: left to the compiler, the wait lands inside the token loop,
+  // where it also waits for the next tile's staging loads once per tile.
+  __builtin_amdgcn_s_waitcnt(0);
 
   const int ntiles = (a.T + TB - 1) / TB;
   SeqStage st;
@@ -198,16 +244,14 @@ __global__ __launch_bounds__(seq_threads<G>()) void seq_kernel(SeqArgs a) {
     const bool more = n + 1 < ntiles;
     if (more) stage_load<G>(st, a, (n + 1) * TB, kh, cb, tid);
     if (n > 0) store_outputs<G>(sm, buf ^ 1, a, (n - 1) * TB, kh, cb, tid);
-    if (computes) compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, m, r, cl);
+    compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, m, r, cl);
     if (more) stage_store<G>(sm, buf ^ 1, st, tid);
     __syncthreads();
   }
   store_outputs<G>(sm, (ntiles - 1) & 1, a, (ntiles - 1) * TB, kh, cb, tid);
 
-  if (computes) {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) a.s_out[(h * kDim + RPL * r + i) * kDim + j] = S[i];
-  }
+  for (int i = 0; i < RPL; ++i) a.s_out[(h * kDim + RPL * r + i) * kDim + j] = S[i];
 }
 
 template <int G>
