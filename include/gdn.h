@@ -157,9 +157,9 @@ int gdn_out_norm(const float* o, const float* z, const float* w, float eps, uint
  * ("#1372 DeltaNet recurrence: STRATA_GDN_CHUNKED=1", sections "What it does" and
  * "Measured": the chunked path loses to the sequential kernel for short prompts, and the
  * pages set a minimum length for it on their card.  On an MI355X the two cross between 48
- * and 64 tokens: 16 tokens take 26 vs 34 us, 32 tokens 30 vs 35 us, 48 tokens 35 vs 37
- * us, 64 tokens 39 vs 37 us, including the launch.)  The workspace may be NULL when
- * T < GDN_CHUNKED_MIN_T.
+ * and 64 tokens: 16 tokens take 29 vs 37 us, 32 tokens 33 vs 37 us, 48 tokens 36 vs 39
+ * us, 64 tokens 40 vs 39 us, 128 tokens 55 vs 44 us, host clock around one call and its
+ * synchronisation.)  The workspace may be NULL when T < GDN_CHUNKED_MIN_T.
  */
 #define GDN_CHUNKED_MIN_T 56
 int gdn_recurrence(const float* q, const float* k, const float* v, const float* g,
