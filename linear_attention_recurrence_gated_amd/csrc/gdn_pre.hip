@@ -16,8 +16,10 @@
 // token's block is one coalesced 512-byte load and one 512-byte store.  The three previous
 // rows of the conv slide along in registers (a run re-reads only the 3 rows before it),
 // the loads of 8 tokens are issued before their arithmetic, and the q/k normalisation is a
-// wave-wide sum (DPP inside each row of 16 lanes, then the four rows' sums read as
-// scalars).  Extra workgroups at the end of the grid form the gate and beta.
+// wave-wide sum (DPP inside each row of 16 lanes and across the rows).  SiLU's sigmoid
+// and the normalisation's reciprocal square root use the hardware's single instructions;
+// the gate and beta, one thread per value, use the exact exp and log1p.  Extra workgroups
+// at the end of the grid form the gate and beta.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -36,17 +38,27 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Sum over the 64 lanes, the same value in every lane (summed in a fixed order).
+constexpr int DPP_ROW_BCAST15 = 0x142;  // row r <- lane 15 of row r - 1 (rows in row_mask)
+constexpr int DPP_ROW_BCAST31 = 0x143;  // rows 2, 3 <- lane 31 (rows in row_mask)
+
+// Sum over the 64 lanes as a wave-uniform value, in a fixed order: each 16-lane row sums
+// itself, then rows 1 and 3 add rows 0 and 2 and row 3 adds lane 31's value, so lane 63
+// holds (s2 + s3) + (s0 + s1).
 __device__ __forceinline__ float wave_sum(float x) {
   x = row16_sum(x);
-  const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-  const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-  const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-  const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-  return (s0 + s1) + (s2 + s3);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                             DPP_ROW_BCAST15, 0xA, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                             DPP_ROW_BCAST31, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
+// u * sigmoid(u) with the sigmoid from the hardware's 2^x and reciprocal (each within about
+// 1 FP32 ulp): far below the tolerance of the step, at a fraction of the exact functions'
+// instructions in a kernel that streams its data once.
+__device__ __forceinline__ float silu(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.44269504088896341f));
+}
 
 __device__ __forceinline__ float softplus(float z) {
   return z > 0.f ? z + log1pf(expf(-z)) : log1pf(expf(z));  // log(1 + e^z)
@@ -103,7 +115,7 @@ __device__ __forceinline__ void conv_run(const PreArgs& a, int hb, int t0, int t
         }
         if (is_q || is_k) {
           const float ss = wave_sum(fmaf(u1, u1, u0 * u0));
-          float r = 1.0f / __fsqrt_rn(ss + a.eps);
+          float r = __builtin_amdgcn_rsqf(ss + a.eps);  // hardware 1/sqrt, within ~1 ulp
           if (is_q) r *= qscale;
           u0 *= r;
           u1 *= r;
