@@ -15,7 +15,9 @@
 // key head, v of a value head) for a run of 64 tokens, two channels per lane, so each
 // token's block is one coalesced 512-byte load and one 512-byte store.  The three previous
 // rows of the conv slide along in registers (a run re-reads only the 3 rows before it),
-// the loads of 8 tokens are issued before their arithmetic, and the q/k normalisation is a
+// the loads of 4 tokens are issued before their arithmetic (measured at T = 32768: 8
+// tokens 3.7 TB/s, 16 tokens 2.9, 4 tokens 4.4, 2 tokens 4.3 -- fewer registers per wave,
+// more waves resident to cover the memory latency), and the q/k normalisation is a
 // wave-wide sum (DPP inside each row of 16 lanes and across the rows).  SiLU's sigmoid
 // and the normalisation's reciprocal square root use the hardware's single instructions;
 // the gate and beta, one thread per value, use the exact exp and log1p.  Extra workgroups
@@ -28,7 +30,7 @@ namespace {
 
 constexpr int PRE_NT = 256;    // 4 waves per workgroup
 constexpr int PRE_RUN = 64;    // tokens per wave
-constexpr int PRE_BATCH = 8;   // tokens whose loads are issued together
+constexpr int PRE_BATCH = 4;   // tokens whose loads are issued together
 
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_mov<DPP_XOR1>(x);
