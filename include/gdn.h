@@ -234,7 +234,8 @@ int gdn_layer_chunked_timed(const float* q, const float* k, const float* v, cons
  *              written.  These six are all given or all NULL (then no gate and beta).
  *   q, k       [T][n_k_heads][dk], v [T][n_v_heads][dv]: written (the recurrence's layout).
  *   eps        >= 0 and finite; activation 0 or 1; dk = dv = 128.  Otherwise, or when the
- *              grid would exceed 2^31 waves, GDN_ERR_BAD_SHAPE.
+ *              grid would reach 2^31 waves or workgroups (one wave per 32 tokens of each
+ *              128-channel head block, one thread per gate value), GDN_ERR_BAD_SHAPE.
  *   T = 0      copies hist_in to hist_out and writes nothing else (every pointer but the
  *              two histories may then be NULL).
  *   No output may overlap an input or another output.  The results are FP32: within a few

@@ -414,6 +414,11 @@ int gdn_pre(const float* x, const float* conv_w, const float* hist_in, float* hi
   if (n_k_heads > 65536 || n_v_heads > 65536) return GDN_ERR_BAD_SHAPE;
   if (activation != 0 && activation != 1) return GDN_ERR_BAD_SHAPE;
   if (!(eps >= 0.0f) || !isfinite(eps)) return GDN_ERR_BAD_SHAPE;
+  // the kernel indexes its waves and workgroups with 32-bit integers (gate workgroups
+  // counted as if the gates were given)
+  int conv_blocks = 0, blocks = 0;
+  if (!gdn::pre_grid(T, n_k_heads, n_v_heads, true, &conv_blocks, &blocks))
+    return GDN_ERR_BAD_SHAPE;
   const size_t f = sizeof(float);
   const size_t C = (size_t)(2 * n_k_heads + n_v_heads) * gdn::kDim;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -446,11 +451,6 @@ int gdn_pre(const float* x, const float* conv_w, const float* hist_in, float* hi
     for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
       if (overlap(out[i], out[j])) return GDN_ERR_ALIASING;
   }
-  // the grid: one wave per (64-token run, 128-channel head block), one thread per gate
-  // (the kernel indexes waves and workgroups with 32-bit integers)
-  const int64_t waves = ((T + 63) / 64) * (int64_t)(2 * n_k_heads + n_v_heads);
-  const int64_t blocks = (waves + 3) / 4 + (gates ? (T * n_v_heads + 255) / 256 : 0);
-  if (waves >= ((int64_t)1 << 31) || blocks >= ((int64_t)1 << 31)) return GDN_ERR_BAD_SHAPE;
   gdn::PreArgs pa{x, conv_w, hist_in, hist_out, gates ? a : nullptr, b, A_log, dt_bias,
                   q, k, v, g, beta, activation, eps, (int)T, n_k_heads, n_v_heads};
   const hipError_t e = gdn::launch_pre(pa, s);

@@ -95,6 +95,10 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_scan_fused(const ChunkArgs& scan, const ChunkArgs* prep_next,
                                    const NormArgs* norm_prev, hipStream_t stream);
 hipError_t launch_out_norm(const NormArgs& a, hipStream_t stream);
+// Grid of the pre kernel (one wave per run of tokens of one 128-channel head block, then
+// one thread per gate value): false if a wave or workgroup index would not fit in 31 bits.
+bool pre_grid(int64_t T, int n_k_heads, int n_v_heads, bool gates, int* conv_blocks,
+              int* blocks);
 hipError_t launch_pre(const PreArgs& a, hipStream_t stream);
 
 }  // namespace gdn

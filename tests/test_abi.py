@@ -254,6 +254,9 @@ def test_pre_validation(L):
     no_gates = dict(a, a=0, b=0, al=0, dt=0, g=0, beta=0)
     assert _pre(L, a, T=-1) == SHAPE
     assert _pre(L, a, T=1 << 31) == SHAPE
+    # one wave per 32 tokens of each of the 80 head blocks: 2^30 tokens need 2^25 * 80 waves
+    assert _pre(L, a, T=1 << 30) == SHAPE
+    assert _pre(L, a, T=1 << 30, Hk=1, Hv=1) != SHAPE  # 2^25 * 3 waves: past the grid check
     assert _pre(L, a, dk=64) == SHAPE
     assert _pre(L, a, Hk=0) == SHAPE
     assert _pre(L, a, activation=2) == SHAPE

@@ -71,10 +71,11 @@ def _compare(x, r, T, activation, eps, gates=True, hk=HK, hv=HV, tag=""):
 
 
 @pytest.mark.parametrize("activation", [0, 1])
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 63, 64, 65, 100, 2049])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 100,
+                               2049])
 def test_pre_against_oracle(T, activation):
-    """Every run length around the 64-token runs and 8-token load batches, from a non-zero
-    history, with and without the activation."""
+    """Run lengths around the 32-token runs of a wave and its 16-token load batches, from a
+    non-zero history, with and without the activation."""
     x = make_pre_inputs(T, seed=T + 7 * activation)
     r = _run_gpu(_dev(x), T, activation, 1e-6)
     _compare(x, r, T, activation, 1e-6)
@@ -107,7 +108,7 @@ def test_pre_extreme_values():
     _compare(x, r, T, 1, 1e-6, tag="extreme")
 
 
-@pytest.mark.parametrize("T1", [1, 2, 3, 64, 100])
+@pytest.mark.parametrize("T1", [1, 2, 3, 16, 31, 32, 33, 64, 100])
 def test_pre_split_calls_bitwise(T1):
     """Two calls chained through the history give one call's bits (every token's arithmetic
     is the same whichever run or call it falls in)."""
