@@ -102,6 +102,15 @@ __device__ __forceinline__ void buf_store(buf_rsrc r, uint32_t byte_off, float v
 __device__ __forceinline__ void buf_store2(buf_rsrc r, uint32_t byte_off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
 }
+// Non-temporal stores (cache policy `nt`): for results that this kernel does not read
+// back, so that they stream out instead of staying dirty in the L2 until the kernel ends.
+constexpr int kCacheNT = 2;
+__device__ __forceinline__ void buf_store_nt(buf_rsrc r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, kCacheNT);
+}
+__device__ __forceinline__ void buf_store2_nt(buf_rsrc r, uint32_t byte_off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, kCacheNT);
+}
 
 // Direct global -> LDS load (gfx950): lane l's 16 bytes at byte_off (from the descriptor's
 // base, checked against its size: out of range reads as 0) land at LDS address
