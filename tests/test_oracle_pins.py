@@ -11,6 +11,7 @@ Sources: "#413 prefill: DeltaNet recurrence with the three value heads of a key 
 thread" (sections "What changes", "Exactness") and "#1372 DeltaNet recurrence:
 STRATA_GDN_CHUNKED=1" (section "What it does").
 """
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -519,3 +520,32 @@ def test_pre_channel_layout(oracle_mod):
             diff = np.abs(r[n] - r0[n]).max(axis=(0, 2))
             for hh in range(diff.size):
                 assert (diff[hh] > 0) == (n == name and hh == head), (c, n, hh)
+
+
+def test_oracle_matches_stored_small_cases():
+    """The oracle's outputs on the three small seeded cases of tests/golden/oracle_small.json
+    (written from the oracle alone by tests/golden/make_oracle_small.py) are unchanged: the
+    y bits exactly, the FP64 values to 1e-13 of each array's largest magnitude."""
+    import json
+    import sys
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    sys.path.insert(0, golden)
+    try:
+        import make_oracle_small as mk
+    finally:
+        sys.path.remove(golden)
+    with open(os.path.join(golden, "oracle_small.json")) as f:
+        stored = json.load(f)["cases"]
+    got = mk.cases()
+    assert set(got) == set(stored)
+    for case, arrays in got.items():
+        assert set(arrays) == set(stored[case]), case
+        for name, a in arrays.items():
+            ref = mk.decode(stored[case][name])
+            a = np.asarray(a)
+            assert a.shape == ref.shape, (case, name)
+            if ref.dtype == np.uint16:
+                assert np.array_equal(a, ref), (case, name)
+            else:
+                scale = float(np.max(np.abs(ref)))
+                assert float(np.max(np.abs(a - ref))) <= 1e-13 * scale, (case, name)
