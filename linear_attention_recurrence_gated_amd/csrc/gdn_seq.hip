@@ -25,6 +25,8 @@
 //  - the inputs of 16 tokens (q/k rows of the key head, the block's v columns, e^{g},
 //    beta and k.q) are staged in double-buffered LDS; the next tile's global loads are in
 //    flight while the current tile computes; one barrier per 16 tokens.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -150,8 +152,6 @@ __device__ __forceinline__ void permlane16_swap(float& x, float& y) {
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
 }
 
-constexpr int DPP_ROW_BCAST15 = 0x142;  // row r <- lane 15 of row r - 1 (rows in row_mask)
-
 // One token of one wave: kc, qc are this token's k and q rows of the lane (already in
 // registers); the next token's rows are read into kn, qn while it computes.
 template <int G>
@@ -173,13 +173,18 @@ __device__ __forceinline__ void token_step(SeqSmem<G>& sm, int buf, int tt, int 
   pq = row16_sum(pq);
   // the two rows of the column: even rows end with S^T k, odd rows with S^T q
   permlane16_swap(pk, pq);  // by row: pk = (pk0, pq0, pk2, pq2), pq = (pk1, pq1, pk3, pq3)
-  const float sum = pk + pq;
-  const float skr = __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, sum),
-                                         __builtin_bit_cast(int, sum), DPP_ROW_BCAST15, 0xA,
-                                         0xF, false));  // S^T k in every row
+  float skr = pk + pq;             // even rows: S^T k, odd rows: S^T q
+  const float esum = ab.x * skr;  // odd rows: e^g S^T q
+  // S^T k into the odd rows too (rows 1 and 3 take lane 15 of rows 0 and 2; rows 0 and 2
+  // keep theirs), in place: written as assembly with `esum` as an input so that the
+  // multiply above is issued first and no copy of the sum is needed (the compiler's own
+  // form kept the sum alive past the broadcast and copied it every token).  The s_nop
+  // gives the two wait states a DPP read needs after a vector-ALU write of its source.
+  asm("s_nop 1\n\tv_mov_b32_dpp %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf"
+      : "+v"(skr)
+      : "v"(esum));
   const float d = ab.y * fmaf(-ab.x, skr, vv);  // beta (v - e^g S^T k)
-  const float om = fmaf(ab.x, sum, d * kq);     // odd rows: (e^g S + k d^T)^T q
+  const float om = fmaf(d, kq, esum);           // odd rows: (e^g S + k d^T)^T q
 #pragma unroll
   for (int i = 0; i < RPL; ++i) S[i] = fmaf((&kc.x)[i], d, ab.x * S[i]);
   sm.o[buf][tt][m][parity][cl] = om;  // the odd row's 16 lanes hold the same value
@@ -239,14 +244,22 @@ __global__ __launch_bounds__(seq_threads<G>()) void seq_kernel(SeqArgs a) {
   stage_load<G>(st, a, 0, kh, cb, tid);
   stage_store<G>(sm, 0, st, tid);
   __syncthreads();
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
+  // Tile n computes from LDS buffer n & 1 while tile n + 1 is staged into the other; the
+  // loop is unrolled over the two buffers so that every LDS address is a per-lane base
+  // plus an immediate (a runtime buffer index costs address arithmetic at every token).
+  auto tile = [&](auto bc, int n) {
+    constexpr int B = decltype(bc)::value;
     const bool more = n + 1 < ntiles;
     if (more) stage_load<G>(st, a, (n + 1) * TB, kh, cb, tid);
-    if (n > 0) store_outputs<G>(sm, buf ^ 1, a, (n - 1) * TB, kh, cb, tid);
-    compute_tile<G>(sm, buf, min(TB, a.T - n * TB), S, m, r, cl);
-    if (more) stage_store<G>(sm, buf ^ 1, st, tid);
+    if (n > 0) store_outputs<G>(sm, B ^ 1, a, (n - 1) * TB, kh, cb, tid);
+    compute_tile<G>(sm, B, min(TB, a.T - n * TB), S, m, r, cl);
+    if (more) stage_store<G>(sm, B ^ 1, st, tid);
     __syncthreads();
+  };
+  for (int n = 0; n < ntiles; n += 2) {
+    tile(std::integral_constant<int, 0>(), n);
+    if (n + 1 >= ntiles) break;
+    tile(std::integral_constant<int, 1>(), n + 1);
   }
   store_outputs<G>(sm, (ntiles - 1) & 1, a, (ntiles - 1) * TB, kh, cb, tid);
 

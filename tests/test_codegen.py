@@ -8,6 +8,10 @@ checked for rules the design relies on:
   scalar-ALU write of m0 needs one wait state before an LDS-DMA load reads it, and the
   compiler's hazard recogniser cannot see inside the inline assembly that issues them, so
   the sequence must carry the wait itself;
+* the cross-lane operations the sequential kernel issues as inline assembly
+  (`v_permlane16_swap_b32`, the in-place `v_mov_b32_dpp ... row_bcast:15`) each carry the
+  two wait states (`s_nop 1`) they need after a vector-ALU write of their operands, since
+  the compiler's hazard recogniser cannot see inside the assembly either;
 * no packed FP32 vector instruction (`v_pk_add_f32`, `v_pk_mul_f32`, `v_pk_fma_f32`)
   appears: the build disables them;
 * no scalar memory store or scalar atomic appears: every store goes through the vector
@@ -89,6 +93,20 @@ def test_every_direct_load_follows_its_m0_write_with_a_wait_state(listings):
                     (name, fn, ins[i - 2][2], line)
                 seen += 1
     assert seen > 0
+
+
+def test_inline_cross_lane_operations_carry_their_wait_states(listings):
+    ins = listings["gdn_seq.hip"]
+    seen = {"v_permlane16_swap_b32": 0, "row_bcast": 0}
+    for i, (fn, op, line) in enumerate(ins):
+        kind = ("v_permlane16_swap_b32" if op == "v_permlane16_swap_b32" else
+                "row_bcast" if op == "v_mov_b32_dpp" and "row_bcast:15" in line else None)
+        if kind is None:
+            continue
+        prev = ins[i - 1][2].split()
+        assert prev[0] == "s_nop" and int(prev[1]) >= 1, (fn, line, ins[i - 1][2])
+        seen[kind] += 1
+    assert all(n > 0 for n in seen.values()), seen
 
 
 def test_no_packed_fp32_vector_instructions(listings):
