@@ -222,6 +222,38 @@ def test_other_group_sizes(kind):
         _check(kind, x, to_dev(x), tag="Hk%d/Hv%d" % (hk, hv))
 
 
+@pytest.mark.parametrize("kind", ["seq", "chunked"])
+def test_more_heads_than_one_wave_of_workgroups(kind):
+    """32 key heads x 96 value heads over two super-blocks: 384 scan workgroups and 512
+    sequential ones, more than the device runs at once, so later workgroups start as
+    earlier ones finish (nothing waits on another workgroup)."""
+    x = make_inputs(2100, seed=96, n_k_heads=32, n_v_heads=96)
+    _check(kind, x, to_dev(x), tag="Hk32/Hv96")
+
+
+def test_layer_more_heads_than_one_wave_of_workgroups():
+    """The one-call layer at 32 x 96 heads: the same bits as the two separate calls, and the
+    norm within 1 fp16 ulp of the oracle's norm of those outputs."""
+    import oracle
+    from linear_attention_recurrence_gated_amd import gdn
+    T, hk, hv = 2100, 32, 96
+    x = make_inputs(T, seed=97, n_k_heads=hk, n_v_heads=hv, with_norm=True)
+    d = to_dev(x)
+    log("layer Hk=%d Hv=%d T=%d" % (hk, hv, T))
+    ws = gdn.workspace(d["q"].device, hk, hv)
+    o1, s1 = gdn.recurrence_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], ws=ws)
+    y1 = gdn.out_norm(o1, d["z"], d["w"], eps=1e-6)
+    torch.cuda.synchronize()
+    y2, o2, s2 = gdn.layer_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["z"],
+                                   d["w"], eps=1e-6, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    y_ref = oracle.out_norm(o2.cpu().numpy(), x["z"], x["w"], 1e-6)
+    assert int(f16_ulp_distance(y2.cpu().numpy(), y_ref).max()) <= 1
+
+
 def test_t8192_seq_and_norm():
     """One layer, T = 8192: sequential recurrence, then the gated RMS norm to FP16."""
     import oracle
