@@ -9,7 +9,7 @@
 // Bound by HBM traffic (read o and z, write y: 1280 bytes per row): each half-wave owns a
 // row (16 bytes of o and of z per lane, one coalesced 512-byte load each), the sum of
 // squares is reduced inside the half-wave with DPP, and a grid-stride loop issues the
-// loads of four rows per half-wave before any arithmetic, with non-temporal (streaming)
+// loads of two rows per half-wave before any arithmetic, with non-temporal (streaming)
 // loads and stores since every byte is touched once.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
@@ -27,7 +27,10 @@ __device__ __forceinline__ void norm_row(const NormArgs& a, int row, int p, cons
                               reinterpret_cast<u32x2*>(a.y + row * kDim + 4 * p));
 }
 
-constexpr int ROWS = 4;  // rows per half-wave per iteration, all loaded before any math
+// rows per half-wave per iteration, all loaded before any math (measured at T = 32768:
+// 1, 2, 3, 4, 6, 8 rows: 391, 382, 390, 397, 428, 464 us; fewer registers per wave leave
+// more waves resident to cover the memory latency)
+constexpr int ROWS = 2;
 
 __global__ __launch_bounds__(NT) void out_norm_kernel(NormArgs a) {
   const int p = threadIdx.x & 31;
