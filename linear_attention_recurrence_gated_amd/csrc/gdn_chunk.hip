@@ -646,9 +646,10 @@ struct FusedArgs {
 
 // The output norm of the previous super-block, run by the three waves of each scan
 // workgroup that the scan leaves free (they share the SIMDs with the compute waves, whose
-// issue their vector instructions delay, so the role keeps its arithmetic to the row's).  They take part in exactly the scan's barriers
-// (one before the first chunk, one per chunk, one after the last), doing a slice of rows between
-// barriers: half-wave `worker` of `nworkers` owns rows worker + j * nworkers, j = 0 .. 127
+// issue their vector instructions delay, so the role keeps its arithmetic to the row's).
+// They take part in exactly the scan's barriers (one before the first chunk, one per
+// chunk, one after the last), doing a slice of rows between barriers: half-wave `worker`
+// of `nworkers` owns rows worker + j * nworkers, j = 0 .. 127
 // (n_scan * 6 * 128 >= 2048 * n_v_heads rows), and handles j = c and j = c + 64 between
 // the barriers of chunks c - 1 and c, with the loads of the next slice issued before the
 // arithmetic of this one.  Slices left over (nch < 64) run before the final barrier.
@@ -687,9 +688,7 @@ __device__ __forceinline__ void norm_role(const NormArgs& n, int worker, int nwo
       const int r = row_of(c + kChunksPerSB * i);
       if (r < n.n_rows)  // whole half-waves: the two halves of a wave may differ
         buf_store2_nt(ry, ((uint32_t)r * kDim + 4 * p) * 2,
-                   gated_rms_row(ov[B][i], zv[B][i],
-                                 wv,
-                                 n.eps));
+                      gated_rms_row(ov[B][i], zv[B][i], wv, n.eps));
     }
   };
   // Slices j .. 63 after the chunks (no barriers), the loads of slice j already in buffer B.
