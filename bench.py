@@ -191,6 +191,12 @@ def _median(xs):
     return sorted(xs)[len(xs) // 2]
 
 
+def _fp32_frac(us_per_token_layer):
+    """F-based TFLOP/s of a recurrence at this µs per token and layer, as a fraction of the
+    FP32 matrix-core peak (the norm and the prep count for nothing)."""
+    return round(FLOP_PER_TOKEN / (us_per_token_layer * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
+
+
 def context_workloads(gdn, d, hip, stream, dev, runs=3):
     """Times (HIP events on the launch stream, medians of `runs` after one unmeasured run)
     of the T = 8192 sequential layer, of the 36-layer stack at T = 2048, and of the step
@@ -220,6 +226,7 @@ def context_workloads(gdn, d, hip, stream, dev, runs=3):
             lay.append(hip.elapsed_ms(evs[0], evs[2]))
         hip.destroy(evs)
     out["seq_recurrence_T8192_us_per_token"] = round(_median(rec) * 1e3 / T8, 6)
+    out["seq_recurrence_T8192_fp32_frac"] = _fp32_frac(_median(rec) * 1e3 / T8)
     out["seq_layer_T8192_us_per_token"] = round(_median(lay) * 1e3 / T8, 6)
     del o8, s8, y8
 
@@ -256,6 +263,7 @@ def context_workloads(gdn, d, hip, stream, dev, runs=3):
         hip.destroy(evs)
     out["stack36_T2048_ms"] = round(_median(stack), 4)
     out["stack36_T2048_us_per_token_layer"] = round(_median(stack) * 1e3 / (L * T2), 6)
+    out["stack36_T2048_fp32_frac"] = _fp32_frac(_median(stack) * 1e3 / (L * T2))
     del layers
     torch.cuda.empty_cache()
 
@@ -457,12 +465,14 @@ def main():
             "recurrence_launches_ms_per_step": round(sum(scan_ms) / n_ev, 4),
             "two_calls_ms": round(two_call_rec_ms + norm_avg_ms, 4),
             "recurrence_only_us_per_token": round(two_call_rec_ms * 1e3 / T, 6),
+            "recurrence_only_fp32_frac": _fp32_frac(two_call_rec_ms * 1e3 / T),
             "standalone_norm_ms": round(norm_avg_ms, 4),
             "standalone_norm_hbm_GBps": round(NORM_BYTES_PER_TOKEN * T / (norm_avg_ms * 1e-3)
                                               / 1e9, 1),
             "standalone_norm_hbm_frac": round(NORM_BYTES_PER_TOKEN * T / (norm_avg_ms * 1e-3)
                                               / 1e9 / PEAK_HBM_GBS, 4),
             "seq_recurrence_us_per_token": round(seq_ms * 1e3 / T, 6),
+            "seq_recurrence_fp32_frac": _fp32_frac(seq_ms * 1e3 / T),
             **ctx,
             "outputs_finite": y_ok,
         },
